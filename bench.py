@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the lightning-attention hot path on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input:
+  * prefill of one MiniMax-like layer: 64 heads x 65,536 tokens, head dim 128, bf16 storage,
+    lambda_h geometric 0.9 -> 0.9999 (outputs + final fp32 states), then
+  * one decode step for 256 sequences x 64 heads with fp32 128x128 states.
+Inputs are resident in HBM before the timed region.  The timed region holds exactly K steps
+bracketed by device synchronisation; per-kernel durations come from HIP events recorded on
+the stream the kernels run on.
+
+Prints ONE JSON line.  Extra legs: the roofline of the dominant kernel (prefill) and the fp64
+CPU oracle timed on a bounded sample of the same workload (--no-cpu-baseline skips it).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + TFLOP/s (% bf16 MFMA peak) H=64 d=128; decode GB/s"
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+T_PREFILL, H, D = 65536, 64, 128
+BT_DECODE = 256
+BLOCK_FLOP_B = 64              # FLOP accounting at block size 64 (the kernel's block size)
+
+
+def prefill_flop(T, H, D, B=BLOCK_FLOP_B):
+    # per token-head: intra 4*B*D (QK^T and PV over full BxB tiles) + inter 2*D^2 + state 2*D^2
+    return T * H * (4 * B * D + 4 * D * D)
+
+
+def prefill_bytes(T, H, D, S=1):
+    # read q, k, v and write out (bf16) + write the fp32 final state
+    return T * H * D * 2 * 4 + S * H * D * D * 4 + H * 4
+
+
+def decode_bytes(Bt, H, D):
+    # state read + write (fp32), q, k, v read and out write (bf16), decay
+    return 2 * Bt * H * D * D * 4 + 4 * Bt * H * D * 2 + H * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
+              "build has no multi-GPU path (heads/sequences would shard with no communication; "
+              "see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_attn_amd as la
+    from long_context_attention_attn_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.workloads()["prefill_64k"]
+    assert (wl.T, wl.H, wl.D) == (T_PREFILL, H, D)
+    q, k, v = wl.inputs(device=dev)
+    decay = wl.decay().to(dev)
+    out = torch.empty_like(q)
+    fs = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    qd, kd, vd = synth.decode_batch(BT_DECODE, H, D, torch.bfloat16, seed=2, device=dev)
+    st = synth.random_state(BT_DECODE, H, D, seed=1, device=dev, scale=0.1)
+    od = torch.empty_like(qd)
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        la.prefill(q, k, v, decay, out=out, final_state=fs)
+        if evs is not None:
+            evs[1].record()
+        la.decode_step(qd, kd, vd, decay, st, out=od)
+        if evs is not None:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    pre_avg = sum(pre_ms) / K
+    dec_avg = sum(dec_ms) / K
+    ms_per_step = wall * 1e3 / K
+
+    tokens_per_step = T_PREFILL + BT_DECODE
+    value = tokens_per_step / (ms_per_step / 1e3)
+    pf = prefill_flop(T_PREFILL, H, D)
+    pb = prefill_bytes(T_PREFILL, H, D)
+    db = decode_bytes(BT_DECODE, H, D)
+    pre_tflops = pf / (pre_avg / 1e3) / 1e12
+    pre_gbps = pb / (pre_avg / 1e3) / 1e9
+    dec_gbps = db / (dec_avg / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "lightning prefill 1 x 65536 tokens x 64 heads x d128 bf16 "
+                        "(lambda 0.9->0.9999, final fp32 states) + decode step 256 seqs x 64 "
+                        "heads fp32 128x128 states",
+            "prefill_tokens": T_PREFILL, "heads": H, "head_dim": D, "block": 64,
+            "decode_batch": BT_DECODE,
+        },
+        "prefill": {
+            "ms": pre_avg, "ms_min": min(pre_ms),
+            "tokens_per_s": T_PREFILL / (pre_avg / 1e3),
+            "tflops": pre_tflops, "pct_bf16_mfma_peak": 100.0 * pre_tflops / BF16_PEAK_TFLOPS,
+            "algorithmic_GBps": pre_gbps,
+            "flop_per_launch": pf, "bytes_per_launch": pb,
+        },
+        "decode": {
+            "ms": dec_avg, "ms_min": min(dec_ms), "GBps": dec_gbps,
+            "pct_hbm_peak": 100.0 * dec_gbps / HBM_PEAK_GBPS, "bytes_per_launch": db,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "prefill_bf16_kernel<128>",
+            "achieved": pre_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": pre_gbps / HBM_PEAK_GBPS, "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(q, k, v, wl, n_tok, tokens_per_step):
+    """The fp64 oracle's recurrent form on the first n_tok tokens of the same input (all 64
+    heads), timed on the host; scaled to tokens/s of the 64-head workload."""
+    import oracle
+
+    o = oracle.default()
+    qs = q[:n_tok].cpu()
+    ks = k[:n_tok].cpu()
+    vs = v[:n_tok].cpu()
+    decay = wl.decay()
+    # Convert outside the timed region (the oracle consumes fp64).
+    from oracle import _f64  # noqa: PLC0415
+
+    qf, kf, vf = _f64(qs), _f64(ks), _f64(vs)
+    t0 = time.perf_counter()
+    o.recurrent(qf, kf, vf, decay.double().numpy())
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_tok / dt, "unit": "tokens/s", "cores": o.num_threads(), "kind": "oracle",
+        "sample": "recurrent fp64 form on the first %d of 65536 tokens, all 64 heads "
+                  "(prefill only; %.1f s)" % (n_tok, dt),
+        "seconds": dt,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,109 @@
+/*
+ * lightning_attn.h -- C ABI of the MI355X (gfx950) lightning-attention forward library.
+ *
+ * The operation.  Lightning attention is causal linear attention computed block by block:
+ * inside a block the left product ((Q K^T) masked) V, across blocks the right product
+ * Q (K^T V) carried by a running d x d state, which avoids the slow cumulative sum
+ * ("MiniMax-01 technical report digest", futurefh.com, section 1 "core innovation"; the
+ * associativity (QK^T)V = Q(K^T V) is stated in the nabfollower blog, section "The Core Tech:
+ * Lightning Attention").  Decode keeps only the fixed-size state and updates it per token
+ * (nabfollower blog, analogy section), and prefill and decode run as separate paths (digest,
+ * section 3 "efficient inference framework").  Packed variable-length batches follow the data
+ * packing of the digest's section 4.  With a constant per-head decay lambda_h (the pages state
+ * none; this library adopts one scalar per head, constant in time), for each packed sequence
+ * and head, with local token index t:
+ *
+ *     S_t = lambda S_{t-1} + k_t^T v_t          (S_{-1} = initial state, or 0)
+ *     o_t = q_t S_t  =  sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s  + lambda^(t+1) q_t S_{-1}
+ *
+ * i.e. the output uses the state that already includes token t.  There is no normaliser, no
+ * feature map and no 1/sqrt(d) scaling inside the operation.
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   activations q, k, v, out : [T][H][D]     (feature index fastest), dtype per la_dtype
+ *   decay                    : [H] float32, lambda_h in [0, 1]
+ *   cu_seqlens               : [S+1] int32,  0 = cu[0] <= cu[1] <= ... <= cu[S] = T
+ *   states                   : [S][H][D][D]  float32, state[a][b] = sum lambda^.. k[a] v[b]
+ *                              (a = key feature, b = value feature)
+ *
+ * Supported: D in {64, 128}; dtype LA_BF16 (bf16 storage, fp32 accumulation, MFMA) or LA_F32
+ * (fp32 storage and arithmetic).  Devices: gfx950 only.
+ *
+ * Ownership and memory.  The caller owns every buffer; the library keeps no pointer after a
+ * call returns and allocates no device memory.  out must not alias q, k or v; state buffers
+ * must not alias anything else.
+ *
+ * Errors.  Argument checks run on the host before any HIP call and return a status; nothing
+ * throws across this ABI.  Device data is not validated: non-monotone cu_seqlens or lambda
+ * outside [0, 1] give undefined results (never an out-of-bounds access for cu values within
+ * [0, T]).  Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream);
+ * LA_ERR_HIP reports a failed HIP call or launch (including "no device").  la_last_error()
+ * gives a human-readable detail for the calling thread's last failure.  Thread-safe.
+ */
+#ifndef LIGHTNING_ATTN_H
+#define LIGHTNING_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1, /* NULL required pointer, negative size, S < 1, H < 1, ...   */
+  LA_ERR_UNSUPPORTED = 2, /* D not in {64,128}, unknown dtype, device not gfx950       */
+  LA_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed / no device    */
+} la_status;
+
+typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define LA_ABI_VERSION 1
+int32_t la_abi_version(void);
+
+/*
+ * Prefill (the block-wise forward pass).
+ *   q, k, v     in  [T][H][D] dtype           (may be NULL when T == 0)
+ *   decay       in  [H] float32
+ *   cu_seqlens  in  [S+1] int32, or NULL meaning one sequence of length T (then S must be 1)
+ *   out         out [T][H][D] dtype           (may be NULL when T == 0)
+ *   final_state out [S][H][D][D] float32, or NULL to skip; an empty sequence gives its
+ *               initial state (or zeros)
+ *   T >= 0 tokens in total, S >= 1 sequences, H >= 1 heads, D head dimension.
+ */
+la_status la_prefill(const void *q, const void *k, const void *v, const float *decay,
+                     const int32_t *cu_seqlens, void *out, float *final_state, int64_t T,
+                     int32_t S, int32_t H, int32_t D, la_dtype dtype, void *stream);
+
+/*
+ * Prefill continuing from a given state per (sequence, head) (chunked prefill; the state
+ * S_{-1} above).  initial_state: [S][H][D][D] float32 or NULL (= zeros).  It may not alias
+ * final_state.  All other arguments as la_prefill.
+ */
+la_status la_prefill_ex(const void *q, const void *k, const void *v, const float *decay,
+                        const int32_t *cu_seqlens, const float *initial_state, void *out,
+                        float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                        la_dtype dtype, void *stream);
+
+/*
+ * One recurrent decode step for Bt independent sequences (one new token each):
+ *   S' = lambda S + k^T v ;  o = q S' ;  state <- S'   (in place)
+ *   q, k, v in [Bt][H][D] dtype; decay [H] float32; state in/out [Bt][H][D][D] float32;
+ *   out [Bt][H][D] dtype.  Bt >= 0 (0 is a no-op).
+ */
+la_status la_decode_step(const void *q, const void *k, const void *v, const float *decay,
+                         float *state, void *out, int32_t Bt, int32_t H, int32_t D,
+                         la_dtype dtype, void *stream);
+
+/* Static string naming a status code. */
+const char *la_status_str(la_status s);
+
+/* Detail of the calling thread's most recent failed call ("" if none). */
+const char *la_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_ATTN_H */

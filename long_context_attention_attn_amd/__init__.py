@@ -1,0 +1,136 @@
+"""MI355X (gfx950) lightning-attention forward: prefill and decode.
+
+Thin Python binding over the C ABI of ``liblightning_attn.so`` (declared in
+``include/lightning_attn.h``).  This module only marshals arguments: it checks tensor
+devices/dtypes/shapes, allocates outputs with torch (device memory), passes raw pointers and
+the current HIP stream, and turns status codes into exceptions.  Every step of the
+computation runs in the library's HIP kernels; there is no other implementation behind these
+functions, and they raise if the compiled library is missing.
+
+Lightning attention ("MiniMax-01 technical report digest", futurefh.com, section 1): causal
+linear attention computed block-wise with an intra-block left product and an inter-block
+right product over a running state; with a constant per-head decay lambda_h,
+    o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s  (+ lambda^(t+1) q_t S0 with an initial state)
+Decode updates the fixed-size state once per token: S' = lambda S + k^T v, o = q S'.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = ["prefill", "decode_step", "LightningAttnError", "library_path"]
+
+LightningAttnError = _lib.LightningAttnError
+library_path = _lib.library_path
+
+_DTYPES = {torch.float32: _lib.LA_F32, torch.bfloat16: _lib.LA_BF16}
+
+
+def _check_act(name, x, dtype, device):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, x.device, device))
+    if x.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, x.dtype, dtype))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_ptr(device) -> int:
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,
+            cu_seqlens: Optional[torch.Tensor] = None, *,
+            initial_state: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None,
+            final_state: Optional[torch.Tensor] = None,
+            return_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Lightning-attention prefill over packed sequences.
+
+    q, k, v: [T, H, D] bf16 or fp32 (same dtype), contiguous, on a gfx950 device.
+    decay: [H] fp32 on the same device.  cu_seqlens: [S+1] int32 on the device, or None for
+    one sequence.  initial_state: optional [S, H, D, D] fp32.  Returns (out [T, H, D],
+    final_state [S, H, D, D] fp32 or None).  Runs asynchronously on the current stream.
+    """
+    device = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, D]")
+    T, H, D = q.shape
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    for name, x in (("k", k), ("v", v)):
+        _check_act(name, x, dtype, device)
+        if x.shape != q.shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(x.shape), tuple(q.shape)))
+    _check_act("q", q, dtype, device)
+    _check_act("decay", decay, torch.float32, device)
+    if decay.shape != (H,):
+        raise ValueError("decay must be [H]")
+    if cu_seqlens is not None:
+        _check_act("cu_seqlens", cu_seqlens, torch.int32, device)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [S+1] with S >= 1")
+        S = cu_seqlens.numel() - 1
+    else:
+        S = 1
+    if initial_state is not None:
+        _check_act("initial_state", initial_state, torch.float32, device)
+        if initial_state.shape != (S, H, D, D):
+            raise ValueError("initial_state must be [S, H, D, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_act("out", out, dtype, device)
+        if out.shape != q.shape:
+            raise ValueError("out must be [T, H, D]")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((S, H, D, D), dtype=torch.float32, device=device)
+    elif final_state is not None:
+        _check_act("final_state", final_state, torch.float32, device)
+        if final_state.shape != (S, H, D, D):
+            raise ValueError("final_state must be [S, H, D, D]")
+    _lib.prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
+                    0 if cu_seqlens is None else cu_seqlens.data_ptr(),
+                    0 if initial_state is None else initial_state.data_ptr(),
+                    out.data_ptr(), 0 if final_state is None else final_state.data_ptr(),
+                    T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
+    return out, final_state
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,
+                state: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent decode step; ``state`` [Bt, H, D, D] fp32 is updated in place.
+
+    q, k, v: [Bt, H, D] bf16 or fp32; decay [H] fp32.  Returns out [Bt, H, D]."""
+    device = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [Bt, H, D]")
+    Bt, H, D = q.shape
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_act(name, x, dtype, device)
+        if x.shape != q.shape:
+            raise ValueError("%s must be [Bt, H, D]" % name)
+    _check_act("decay", decay, torch.float32, device)
+    if decay.shape != (H,):
+        raise ValueError("decay must be [H]")
+    _check_act("state", state, torch.float32, device)
+    if state.shape != (Bt, H, D, D):
+        raise ValueError("state must be [Bt, H, D, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_act("out", out, dtype, device)
+        if out.shape != q.shape:
+            raise ValueError("out must be [Bt, H, D]")
+    _lib.decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(), state.data_ptr(),
+                     out.data_ptr(), Bt, H, D, _DTYPES[dtype], _stream_ptr(device))
+    return out

@@ -1,0 +1,157 @@
+// la_api.hip -- C-ABI front end: argument validation, device check, dispatch, status codes.
+// The operation and the contract of every entry point are documented in lightning_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "la_internal.h"
+#include "lightning_attn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+la_status fail(la_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+la_status fail(la_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];  // 1 = gfx950, 0 = other arch
+
+// Checks that the current device exists and is a gfx950; cached per device.
+la_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LA_ERR_HIP, "device index %d out of range", dev);
+  hipError_t perr = hipSuccess;
+  std::call_once(g_dev_once[dev], [&]() {
+    hipDeviceProp_t prop;
+    perr = hipGetDeviceProperties(&prop, dev);
+    g_dev_ok[dev] = (perr == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0);
+  });
+  if (perr != hipSuccess)
+    return fail(LA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(perr));
+  if (!g_dev_ok[dev]) return fail(LA_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+  return LA_OK;
+}
+
+la_status check_common(const void *q, const void *k, const void *v, const float *decay,
+                       const void *out, int64_t ntok, int32_t H, int32_t D, la_dtype dtype) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (D != 64 && D != 128) return fail(LA_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", D);
+  if (H < 1) return fail(LA_ERR_INVALID_ARG, "H = %d < 1", H);
+  if (ntok < 0) return fail(LA_ERR_INVALID_ARG, "negative token count %lld", (long long)ntok);
+  if (decay == nullptr) return fail(LA_ERR_INVALID_ARG, "decay is NULL");
+  if (ntok > 0) {
+    if (!q || !k || !v || !out) return fail(LA_ERR_INVALID_ARG, "q, k, v or out is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+      return fail(LA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (ntok > (int64_t(1) << 40) / ((int64_t)H * D))
+      return fail(LA_ERR_INVALID_ARG, "tensor too large");
+  }
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t la_abi_version(void) { return LA_ABI_VERSION; }
+
+const char *la_status_str(la_status s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+  }
+  return "LA_ERR_UNKNOWN";
+}
+
+const char *la_last_error(void) { return g_err; }
+
+la_status la_prefill_ex(const void *q, const void *k, const void *v, const float *decay,
+                        const int32_t *cu_seqlens, const float *initial_state, void *out,
+                        float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                        la_dtype dtype, void *stream) {
+  g_err[0] = '\0';
+  la_status st = check_common(q, k, v, decay, out, T, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
+  if (cu_seqlens == nullptr && S != 1)
+    return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
+  if ((long long)S * H * (D / 32) > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "S*H too large");
+  if (initial_state != nullptr && initial_state == final_state)
+    return fail(LA_ERR_INVALID_ARG, "initial_state aliases final_state");
+  if (final_state == nullptr && (T == 0)) return LA_OK;  // nothing to compute or write
+  st = check_device();
+  if (st != LA_OK) return st;
+
+  LaPrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.cu_seqlens = cu_seqlens;
+  a.initial_state = initial_state;
+  a.out = out;
+  a.final_state = final_state;
+  a.T = T;
+  a.S = S;
+  a.H = H;
+  a.D = D;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dtype == LA_BF16 ? la_launch_prefill_bf16(a, s) : la_launch_prefill_f32(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return LA_OK;
+}
+
+la_status la_prefill(const void *q, const void *k, const void *v, const float *decay,
+                     const int32_t *cu_seqlens, void *out, float *final_state, int64_t T,
+                     int32_t S, int32_t H, int32_t D, la_dtype dtype, void *stream) {
+  return la_prefill_ex(q, k, v, decay, cu_seqlens, nullptr, out, final_state, T, S, H, D, dtype,
+                       stream);
+}
+
+la_status la_decode_step(const void *q, const void *k, const void *v, const float *decay,
+                         float *state, void *out, int32_t Bt, int32_t H, int32_t D,
+                         la_dtype dtype, void *stream) {
+  g_err[0] = '\0';
+  la_status st = check_common(q, k, v, decay, out, Bt, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (Bt == 0) return LA_OK;
+  if (state == nullptr) return fail(LA_ERR_INVALID_ARG, "state is NULL");
+  if (!aligned16(state)) return fail(LA_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  if ((long long)Bt * H > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "Bt*H too large");
+  st = check_device();
+  if (st != LA_OK) return st;
+  LaDecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.state = state;
+  a.out = out;
+  a.Bt = Bt;
+  a.H = H;
+  a.D = D;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dtype == LA_BF16 ? la_launch_decode_bf16(a, s) : la_launch_decode_f32(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return LA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+* the shared library loads and exports every function include/lightning_attn.h declares;
+* argument validation returns the documented status codes before any HIP call;
+* on a machine without a GPU, a well-formed call reports LA_ERR_HIP (no device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from long_context_attention_attn_amd import _lib
+
+    if not os.path.exists(_lib.library_path()):
+        from long_context_attention_attn_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    from long_context_attention_attn_amd import _lib
+
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), "missing export %s" % name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.la_abi_version() == 1
+    assert lib.la_status_str(0) == b"LA_OK"
+    assert lib.la_status_str(1) == b"LA_ERR_INVALID_ARG"
+    assert lib.la_status_str(2) == b"LA_ERR_UNSUPPORTED"
+    assert lib.la_status_str(3) == b"LA_ERR_HIP"
+    assert lib.la_status_str(99) == b"LA_ERR_UNKNOWN"
+
+
+# Fake, never-dereferenced 16-byte aligned "device" addresses for validation-only calls.
+P = ctypes.c_void_p(0x100000)
+P2 = ctypes.c_void_p(0x200000)
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def _prefill(lib, q=P, k=P, v=P, decay=P, cu=None, out=P2, fs=None, T=64, S=1, H=2, D=128,
+             dt=1, init=None):
+    return lib.la_prefill_ex(q, k, v, decay, cu, init, out, fs, T, S, H, D, dt, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(D=96), 2), (dict(D=32), 2), (dict(dt=7), 2),
+    (dict(H=0), 1), (dict(T=-1), 1), (dict(S=0), 1), (dict(S=2), 1),  # S=2 without cu_seqlens
+    (dict(q=None), 1), (dict(out=None), 1), (dict(decay=None), 1),
+    (dict(q=MISALIGNED), 1), (dict(init=P2, fs=P2), 1),
+])
+def test_prefill_validation(lib, kwargs, status):
+    assert _prefill(lib, **kwargs) == status
+    assert lib.la_last_error() != b""
+
+
+def test_prefill_empty_is_noop(lib):
+    # T = 0 and no final state requested: nothing to do, no HIP call.
+    assert _prefill(lib, q=None, k=None, v=None, out=None, T=0) == 0
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(D=100), 2), (dict(H=0), 1), (dict(Bt=-3), 1), (dict(state=None), 1),
+    (dict(state=MISALIGNED), 1), (dict(q=None), 1),
+])
+def test_decode_validation(lib, kwargs, status):
+    a = dict(q=P, k=P, v=P, decay=P, state=P2, out=P, Bt=4, H=2, D=128, dt=1)
+    a.update(kwargs)
+    rc = lib.la_decode_step(a["q"], a["k"], a["v"], a["decay"], a["state"], a["out"], a["Bt"],
+                            a["H"], a["D"], a["dt"], None)
+    assert rc == status
+
+
+def test_decode_zero_batch_is_noop(lib):
+    assert lib.la_decode_step(None, None, None, P, None, None, 0, 2, 128, 1, None) == 0
+
+
+def test_no_device_reports_hip_error(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    # Well-formed arguments: validation passes, the device check fails.
+    assert _prefill(lib) == 3
+    assert b"hip" in lib.la_last_error().lower()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    import long_context_attention_attn_amd as la
+
+    q = torch.zeros(8, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        la.prefill(q, q, q.to(torch.float32), torch.ones(1))

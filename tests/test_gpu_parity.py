@@ -1,0 +1,216 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by element
+on seeded inputs, at sizes the oracle finishes in seconds that span several 64-token blocks and
+ragged tails; plus bitwise invariants of the GPU path itself.
+
+Tolerances: relative L2 error per (sequence, head) slice <= 2e-2 for bf16 storage (fp32
+accumulation) and <= 1e-4 for fp32 storage.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_attn_amd as la
+import oracle
+from gpu_util import BF16_TOL, F32_TOL, banner, dev, slice_errors, state_errors, to_np
+from long_context_attention_attn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: BF16_TOL, torch.float32: F32_TOL}
+
+
+def _run_prefill(q, k, v, decay, cu=None, init=None):
+    d = dev()
+    out, fs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d),
+                         None if cu is None else cu.to(d),
+                         initial_state=None if init is None else init.to(d))
+    torch.cuda.synchronize()
+    return out, fs
+
+
+def test_tiny_fp32_no_decay():
+    """1 x 256 tokens, 1 head, D=64, fp32, lambda = 1; full quadratic oracle."""
+    wl = synth.workloads()["tiny_fp32"]
+    banner("tiny_fp32 T=256 H=1 D=64 fp32")
+    q, k, v = wl.inputs()
+    decay = wl.decay()
+    out, fs = _run_prefill(q, k, v, decay)
+    ref = oracle.quadratic(q, k, v, decay)
+    ref_s = oracle.final_state(k, v, decay)
+    e = slice_errors(to_np(out), ref, [0, 256]).max()
+    es = state_errors(to_np(fs), ref_s).max()
+    print("tiny fp32: out %.2e state %.2e" % (e, es))
+    assert e <= F32_TOL and es <= F32_TOL
+
+
+RAGGED = [1, 63, 64, 65, 0, 130, 200, 7]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("with_init", [False, True], ids=["zero_state", "init_state"])
+def test_ragged_varlen(dtype, D, with_init):
+    """Packed sequences of lengths 1, 63, 64, 65, 0, 130, 200, 7 (empty one included), three
+    heads with lambda = 0, 0.95, 1; full quadratic oracle on every row."""
+    banner("ragged varlen dtype=%s D=%d init=%s" % (dtype, D, with_init))
+    H = 3
+    cu = synth.cu_from_lengths(RAGGED)
+    q, k, v = synth.qkv(int(cu[-1]), H, D, dtype, seed=3)
+    decay = torch.tensor([0.0, 0.95, 1.0], dtype=torch.float32)
+    init = synth.random_state(len(RAGGED), H, D, seed=4, scale=0.1) if with_init else None
+    out, fs = _run_prefill(q, k, v, decay, cu, init)
+    ref = oracle.quadratic(q, k, v, decay, cu, init_state=init)
+    ref_s = oracle.final_state(k, v, decay, cu, init_state=init)
+    e = slice_errors(to_np(out), ref, cu)
+    es = state_errors(to_np(fs), ref_s)
+    print("ragged: max out %.2e max state %.2e" % (e.max(), es.max()))
+    assert e.max() <= TOL[dtype] and es.max() <= TOL[dtype]
+    if not with_init:
+        assert torch.count_nonzero(fs[4]).item() == 0  # empty sequence -> zero state
+    else:
+        assert torch.equal(fs[4].cpu(), init[4])       # empty sequence -> its initial state
+
+
+def test_prefill_8k_full_quadratic():
+    """8 heads x 8192 tokens, D=128, bf16, lambda geometric 0.9 -> 0.999; every row checked
+    against the quadratic oracle."""
+    wl = synth.workloads()["prefill_8k"]
+    banner("prefill_8k T=8192 H=8 D=128 bf16")
+    q, k, v = wl.inputs()
+    decay = wl.decay()
+    out, fs = _run_prefill(q, k, v, decay)
+    ref = oracle.quadratic(q, k, v, decay)
+    ref_s = oracle.final_state(k, v, decay)
+    e = slice_errors(to_np(out), ref, [0, wl.T])
+    es = state_errors(to_np(fs), ref_s)
+    print("prefill_8k per-head out errors:", np.array2string(e[0], precision=2))
+    print("prefill_8k per-head state errors:", np.array2string(es[0], precision=2))
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
+
+
+def test_determinism_bitwise():
+    """Two runs on the same inputs give bit-identical outputs and states."""
+    banner("determinism T=4100 H=8 D=128 bf16")
+    q, k, v = synth.qkv(4100, 8, 128, torch.bfloat16, seed=5)
+    decay = synth.decay_geometric(8, 0.9, 0.9999)
+    o1, s1 = _run_prefill(q, k, v, decay)
+    o2, s2 = _run_prefill(q, k, v, decay)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_causality_bitwise(dtype):
+    """Replacing every token from t0 = 150 on (inside a 64-token block) by other finite values
+    leaves the outputs of tokens < t0 bit-identical."""
+    banner("causality dtype=%s" % dtype)
+    T, H, D, t0 = 300, 4, 128, 150
+    q, k, v = synth.qkv(T, H, D, dtype, seed=6)
+    q2, k2, v2 = synth.qkv(T, H, D, dtype, seed=7)
+    decay = synth.decay_geometric(H, 0.9, 0.999)
+    qa, ka, va = q.clone(), k.clone(), v.clone()
+    qa[t0:], ka[t0:], va[t0:] = q2[t0:], k2[t0:], v2[t0:]
+    o1, _ = _run_prefill(q, k, v, decay)
+    o2, _ = _run_prefill(qa, ka, va, decay)
+    assert torch.equal(o1[:t0], o2[:t0])
+    assert not torch.equal(o1[t0:], o2[t0:])
+
+
+def test_varlen_packing_bitwise():
+    """A packed varlen call equals separate calls per sequence, bit for bit."""
+    banner("varlen packing bitwise")
+    lengths = [100, 1, 64, 250]
+    H, D = 4, 128
+    cu = synth.cu_from_lengths(lengths)
+    q, k, v = synth.qkv(sum(lengths), H, D, torch.bfloat16, seed=8)
+    decay = synth.decay_geometric(H, 0.9, 0.999)
+    out, fs = _run_prefill(q, k, v, decay, cu)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        o1, s1 = _run_prefill(q[a:b].contiguous(), k[a:b].contiguous(), v[a:b].contiguous(), decay)
+        assert torch.equal(out[a:b], o1), "sequence %d" % s
+        assert torch.equal(fs[s], s1[0]), "state %d" % s
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_step_vs_oracle(dtype, D):
+    """One decode step on seeded random states for 8 sequences x 4 heads."""
+    banner("decode dtype=%s D=%d" % (dtype, D))
+    Bt, H = 8, 4
+    q, k, v = synth.decode_batch(Bt, H, D, dtype, seed=9)
+    decay = torch.tensor([0.0, 0.5, 0.99, 1.0], dtype=torch.float32)
+    st0 = synth.random_state(Bt, H, D, seed=10, scale=0.3)
+    st = st0.to(dev())
+    out = la.decode_step(q.to(dev()), k.to(dev()), v.to(dev()), decay.to(dev()), st)
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle.decode_step(q, k, v, decay, st0)
+    e = max(float(np.linalg.norm(to_np(out)[b, h] - ref_o[b, h]) / np.linalg.norm(ref_o[b, h]))
+            for b in range(Bt) for h in range(H))
+    es = state_errors(to_np(st), ref_s).max()
+    print("decode: out %.2e state %.2e" % (e, es))
+    assert e <= TOL[dtype]
+    assert es <= 1e-6  # fp32 state, one fused multiply-add per element
+
+
+def test_prefill_then_decode_matches_longer_prefill():
+    """prefill(n) then decode(token n) equals prefill(n+1): last row and state (GPU vs GPU and
+    GPU vs oracle)."""
+    banner("prefill -> decode consistency")
+    n, H, D = 129, 4, 128
+    q, k, v = synth.qkv(n + 1, H, D, torch.bfloat16, seed=11)
+    decay = synth.decay_geometric(H, 0.9, 0.999)
+    _, s_n = _run_prefill(q[:n].contiguous(), k[:n].contiguous(), v[:n].contiguous(), decay)
+    st = s_n[0].unsqueeze(0).clone()
+    od = la.decode_step(q[n:].to(dev()), k[n:].to(dev()), v[n:].to(dev()), decay.to(dev()), st)
+    o_full, s_full = _run_prefill(q, k, v, decay)
+    torch.cuda.synchronize()
+    ref = oracle.quadratic(q, k, v, decay)
+    for h in range(H):
+        a = to_np(od)[0, h]
+        assert np.linalg.norm(a - to_np(o_full)[n, h]) <= BF16_TOL * np.linalg.norm(ref[n, h])
+        assert np.linalg.norm(a - ref[n, h]) <= BF16_TOL * np.linalg.norm(ref[n, h])
+    assert state_errors(to_np(st), to_np(s_full)).max() <= BF16_TOL
+
+
+def test_chunked_prefill_matches_whole():
+    """prefill of [0, m) then prefill_ex of [m, n) from its state equals the whole prefill."""
+    banner("chunked prefill")
+    n, m, H, D = 333, 150, 4, 128
+    q, k, v = synth.qkv(n, H, D, torch.bfloat16, seed=12)
+    decay = synth.decay_geometric(H, 0.9, 0.999)
+    o_all, s_all = _run_prefill(q, k, v, decay)
+    _, s_m = _run_prefill(q[:m].contiguous(), k[:m].contiguous(), v[:m].contiguous(), decay)
+    o_tail, s_tail = _run_prefill(q[m:].contiguous(), k[m:].contiguous(), v[m:].contiguous(),
+                                  decay, init=s_m.cpu())
+    ref = oracle.quadratic(q, k, v, decay)
+    e = slice_errors(to_np(o_tail), ref[m:], [0, n - m]).max()
+    assert e <= BF16_TOL
+    assert slice_errors(to_np(o_tail), to_np(o_all)[m:], [0, n - m]).max() <= BF16_TOL
+    assert state_errors(to_np(s_tail), to_np(s_all)).max() <= BF16_TOL
+
+
+def test_all_empty_sequences():
+    """T = 0 with two empty sequences: final states are zero, or the initial states."""
+    banner("all-empty sequences")
+    H, D = 2, 128
+    cu = torch.tensor([0, 0, 0], dtype=torch.int32, device=dev())
+    e = torch.empty((0, H, D), dtype=torch.bfloat16, device=dev())
+    decay = torch.full((H,), 0.9, device=dev())
+    _, fs = la.prefill(e, e, e, decay, cu)
+    init = torch.randn((2, H, D, D), device=dev())
+    _, fs2 = la.prefill(e, e, e, decay, cu, initial_state=init)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fs).item() == 0
+    assert torch.equal(fs2, init)
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129])
+def test_single_head_lengths(n):
+    """H = 1 at block-boundary lengths."""
+    banner("single head n=%d" % n)
+    q, k, v = synth.qkv(n, 1, 128, torch.bfloat16, seed=13 + n)
+    decay = torch.tensor([0.97])
+    out, fs = _run_prefill(q, k, v, decay)
+    ref = oracle.quadratic(q, k, v, decay)
+    assert slice_errors(to_np(out), ref, [0, n]).max() <= BF16_TOL
+    assert state_errors(to_np(fs), oracle.final_state(k, v, decay)).max() <= BF16_TOL

@@ -1,0 +1,106 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times:
+
+* 64 heads x 65,536 tokens (one MiniMax-like layer): every output and state of all heads
+  against the oracle's recurrent form, plus sampled rows against the quadratic form;
+* 16 packed sequences of 1,024..32,768 tokens x 64 heads: heads {0, 21, 42, 63} of every
+  sequence against the recurrent form;
+* 1,048,576 tokens x 64 heads (int64 indexing: T*H*D > 2^31): heads {0, 21, 42, 63} against
+  the recurrent form;
+* one decode step for 256 sequences x 64 heads of fp32 128x128 states: every pair.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_attn_amd as la
+import oracle
+from gpu_util import BF16_TOL, banner, dev, rel, slice_errors, state_errors, to_np
+from long_context_attention_attn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SAMPLED_HEADS = [0, 21, 42, 63]
+
+
+def _heads(x, heads):
+    return x[:, heads, :].contiguous().cpu()
+
+
+def test_prefill_64k_all_heads():
+    wl = synth.workloads()["prefill_64k"]
+    banner("prefill_64k T=65536 H=64 D=128 bf16 (GPU inputs)")
+    q, k, v = wl.inputs(device="cuda")
+    decay = wl.decay()
+    out, fs = la.prefill(q, k, v, decay.to(dev()))
+    torch.cuda.synchronize()
+    worst, worst_s = 0.0, 0.0
+    for h0 in range(0, wl.H, 16):
+        hs = list(range(h0, h0 + 16))
+        qh, kh, vh = _heads(q, hs), _heads(k, hs), _heads(v, hs)
+        ref, ref_s = oracle.recurrent(qh, kh, vh, decay[hs])
+        e = slice_errors(to_np(_heads(out, hs)), ref, [0, wl.T])
+        es = state_errors(to_np(fs[:, hs]), ref_s)
+        worst, worst_s = max(worst, e.max()), max(worst_s, es.max())
+        print("heads %d..%d: out %.2e state %.2e" % (h0, h0 + 15, e.max(), es.max()), flush=True)
+    # Sampled rows against the quadratic (definition) form on all heads.
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 63, 64, 65, 4095, 4096, wl.T - 1] +
+                      [int(x) for x in rng.integers(0, wl.T, 24)]))
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    refr = oracle.quadratic_rows(qc, kc, vc, decay, rows)
+    got = to_np(out[rows])
+    for h in range(wl.H):
+        assert rel(got[:, h], refr[:, h]) <= BF16_TOL, "row sample head %d" % h
+    print("prefill_64k: worst out %.2e worst state %.2e" % (worst, worst_s))
+    assert worst <= BF16_TOL and worst_s <= BF16_TOL
+
+
+def test_varlen_16_sampled_heads():
+    wl = synth.workloads()["varlen_16"]
+    banner("varlen_16 T=%d S=16 H=64 D=128 bf16 (GPU inputs)" % wl.T)
+    q, k, v = wl.inputs(device="cuda")
+    decay = wl.decay()
+    cu = wl.cu_seqlens()
+    out, fs = la.prefill(q, k, v, decay.to(dev()), cu.to(dev()))
+    torch.cuda.synchronize()
+    hs = SAMPLED_HEADS
+    ref, ref_s = oracle.recurrent(_heads(q, hs), _heads(k, hs), _heads(v, hs), decay[hs], cu)
+    e = slice_errors(to_np(_heads(out, hs)), ref, cu)
+    es = state_errors(to_np(fs[:, hs]), ref_s)
+    print("varlen_16: out %.2e state %.2e" % (e.max(), es.max()))
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
+
+
+def test_prefill_1m_sampled_heads():
+    wl = synth.workloads()["prefill_1m"]
+    banner("prefill_1m T=1048576 H=64 D=128 bf16 (GPU inputs)")
+    q, k, v = wl.inputs(device="cuda")
+    decay = wl.decay()
+    out, fs = la.prefill(q, k, v, decay.to(dev()))
+    torch.cuda.synchronize()
+    hs = SAMPLED_HEADS
+    qh, kh, vh, oh = _heads(q, hs), _heads(k, hs), _heads(v, hs), _heads(out, hs)
+    del q, k, v, out
+    ref, ref_s = oracle.recurrent(qh, kh, vh, decay[hs])
+    e = slice_errors(to_np(oh), ref, [0, wl.T])
+    es = state_errors(to_np(fs[:, hs]), ref_s)
+    print("prefill_1m: out", np.array2string(e[0], precision=2), "state",
+          np.array2string(es[0], precision=2))
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
+
+
+def test_decode_256x64():
+    banner("decode Bt=256 H=64 D=128 bf16, fp32 states")
+    Bt, H, D = 256, 64, 128
+    q, k, v = synth.decode_batch(Bt, H, D, torch.bfloat16, seed=2)
+    decay = synth.decay_geometric(H, 0.9, 0.9999)
+    st0 = synth.random_state(Bt, H, D, seed=1, scale=0.1)
+    st = st0.to(dev())
+    out = la.decode_step(q.to(dev()), k.to(dev()), v.to(dev()), decay.to(dev()), st)
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle.decode_step(q, k, v, decay, st0)
+    got = to_np(out)
+    e = max(rel(got[b, h], ref_o[b, h]) for b in range(Bt) for h in range(H))
+    es = float(np.abs(to_np(st) - ref_s).max() / np.abs(ref_s).max())
+    print("decode_256x64: out %.2e state(max-abs rel) %.2e" % (e, es))
+    assert e <= BF16_TOL and es <= 1e-6
