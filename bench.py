@@ -54,7 +54,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, time a plain device-to-device copy of this "
+                         "many MiB (K times); used to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
@@ -69,6 +72,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps, args.warmup)
+        return
     wl = synth.workloads()["prefill_64k"]
     assert (wl.T, wl.H, wl.D) == (T_PREFILL, H, D)
     q, k, v = wl.inputs(device=dev)
@@ -158,6 +164,27 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)
     print(json.dumps(result), flush=True)
+
+
+def copy_probe(mib, steps, warmup):
+    """A plain copy of `mib` MiB between two device buffers (read mib, write mib)."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "ms": ms, "GBps": 2 * n / (ms / 1e3) / 1e9}), flush=True)
 
 
 def cpu_baseline(q, k, v, wl, n_tok, tokens_per_step):

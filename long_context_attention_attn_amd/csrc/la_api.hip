@@ -53,6 +53,7 @@ la_status check_common(const void *q, const void *k, const void *v, const float 
   if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (D != 64 && D != 128) return fail(LA_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", D);
   if (H < 1) return fail(LA_ERR_INVALID_ARG, "H = %d < 1", H);
+  if (H > 65536) return fail(LA_ERR_INVALID_ARG, "H = %d > 65536", H);
   if (ntok < 0) return fail(LA_ERR_INVALID_ARG, "negative token count %lld", (long long)ntok);
   if (decay == nullptr) return fail(LA_ERR_INVALID_ARG, "decay is NULL");
   if (ntok > 0) {

@@ -12,21 +12,25 @@
 //
 // which is exact algebra for o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s.
 //
-// Work decomposition (one fused pass, one HBM read of q/k/v and one write of out):
+// Work decomposition (one fused pass: one HBM read of q/k/v, one write of out):
 //   * one workgroup per (sequence, head, 32-column slice of the value dimension).  Value
 //     columns are independent: KV[:, c] and O[:, c] depend on V[:, c] only.  The D/32 slices
 //     of one head read the same Q and K blocks, so the workgroup index is mapped so that they
 //     land on the same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
-//   * 4 waves; wave w owns output rows 16w..16w+15 of each block and state rows
-//     [w*D/4, (w+1)*D/4) of the fp32 state, held in MFMA accumulators across the whole loop.
-//   * per block and wave: S^T = K Q^T tiles (causal: tiles 0..w only), decay mask applied in
-//     registers; the S^T accumulator layout is exactly the B-operand layout of P for
-//     O^T += V^T P^T, so P never leaves registers.  O^T = KV^T Q^T (inter) uses the bf16 copy
-//     of the previous state shared through LDS.  The state update K^T (Lambda V) reads K and V
-//     token-major through ds_read_b64_tr_b16 (LDS transpose reads), so the tiles are staged
-//     in LDS once, in their natural row-major layout.
-//   * q/k/v blocks are prefetched two blocks ahead into registers and written to a
-//     double-buffered LDS stage; one barrier per block.
+//   * 4 waves, one per SIMD.  Wave w owns output rows 16w..16w+15 of each block; its causal
+//     score work grows with w (w+1 score tiles), so the fp32 state rows, held in MFMA
+//     accumulators for the whole sequence, are dealt unevenly (more to the low waves) to even
+//     out the MFMA count per wave.  Each wave's role is a template parameter, so every loop
+//     trip count is static and the code between barriers is straight-line.
+//   * per block and wave: S^T = K Q^T tiles, decay mask applied in registers; the S^T
+//     accumulator layout is exactly the B-operand layout of P for O^T += V^T P^T, so P never
+//     leaves registers.  O^T = KV^T Q^T (inter) reads a bf16 copy of the previous state shared
+//     through LDS.  The state update K^T (Lambda V) reads K and V token-major through
+//     ds_read_b64_tr_b16 (LDS transpose reads), so tiles are staged once, row-major.
+//   * q/k/v blocks are fetched with buffer loads two blocks ahead into registers and written
+//     to a double-buffered LDS stage; one barrier per block.  Buffer range checking zero-fills
+//     rows past the end of a sequence and drops stores past it, so there are no branches
+//     around memory operations (which lets the compiler wait on exactly the loads it needs).
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l (g = l/16, c = l%16) holds A[c][k in K(g)],
 // B[k in K(g)][c] and C[4g+i][c], i = 0..3; any k-assignment K(g) shared by A and B gives
@@ -39,12 +43,15 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BLK = 64;   // tokens per block
 constexpr int CV = 32;    // value columns per workgroup
 constexpr int NTHR = 256; // 4 waves
 constexpr int PAD = 8;    // bf16 padding per LDS row (keeps 16-byte alignment, spreads banks)
+constexpr int RSRC_WORD3 = 0x00020000;  // buffer descriptor dword 3 for raw 32-bit accesses
 
 template <int D>
 struct Cfg {
@@ -54,7 +61,6 @@ struct Cfg {
   static constexpr int QK_LOADS = BLK * CHUNKS / NTHR;    // chunks per thread per tensor
   static constexpr int ROWS_PER_LOAD = NTHR / CHUNKS;
   static constexpr int KSTEPS = D / 32;                   // MFMA k-steps over features
-  static constexpr int RT = D / 64;                       // 16-row state tiles per wave
   static constexpr int STAGE_QK = BLK * QROW;
   static constexpr int STAGE_V = BLK * VROW;
   static constexpr int STAGE = 2 * STAGE_QK + STAGE_V;    // Q, K, V of one block
@@ -62,11 +68,23 @@ struct Cfg {
   static constexpr int SMEM = 2 * STAGE + 2 * KVX;
 };
 
+// State rows (16-row tiles) owned by wave W, and the first owned row.  Low waves do fewer
+// causal score tiles, so they take more state tiles.
+template <int D, int W>
+struct Own {
+  static constexpr int T128[4] = {3, 3, 1, 1};
+  static constexpr int T64[4] = {2, 1, 1, 0};
+  static constexpr int tiles(int w) { return D == 128 ? T128[w] : T64[w]; }
+  static constexpr int first(int w) { return w == 0 ? 0 : first(w - 1) + 16 * tiles(w - 1); }
+  static constexpr int RT = tiles(W);
+  static constexpr int DK0 = first(W);
+};
+
 template <int D>
 struct Regs {
-  uint4 q[Cfg<D>::QK_LOADS];
-  uint4 k[Cfg<D>::QK_LOADS];
-  uint4 v;
+  u32x4 q[Cfg<D>::QK_LOADS];
+  u32x4 k[Cfg<D>::QK_LOADS];
+  u32x4 v;
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -82,6 +100,11 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   return r;
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           RSRC_WORD3);
+}
+
 // Transpose read: within each 16-lane group, lane c receives element c of the four 4-element
 // pieces addressed by lanes 4e + c/4 (e = 0..3).  With lane s pointing at row base + s/4,
 // column col0 + 4*(s%4) of a row-major tile, lane c receives rows base..base+3 of column
@@ -91,31 +114,38 @@ __device__ __forceinline__ bf16x4 tr_read(const __bf16 *p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// Everything a wave needs about its workgroup's chain.
+struct Chain {
+  const __bf16 *q, *k, *v;
+  __bf16 *out;
+  int64_t tok0;  // first token of the sequence
+  int64_t n;     // its length
+  int nb;        // number of blocks
+  int H, h, c0;  // heads, this head, first value column of the slice
+};
+
+// Fetch block `blk` of the chain into registers.  Rows at or past the end of the sequence
+// (and whole blocks past the end) read as zero through buffer range checking.
 template <int D>
-__device__ __forceinline__ void load_block(Regs<D> &r, const __bf16 *__restrict__ q,
-                                           const __bf16 *__restrict__ k,
-                                           const __bf16 *__restrict__ v, int64_t tok, int b,
-                                           int H, int h, int c0, int tid) {
+__device__ __forceinline__ void load_block(Regs<D> &r, const Chain &c, int blk, int tid) {
   using C = Cfg<D>;
+  const int64_t rem = c.n - (int64_t)blk * BLK;
+  const int b = rem <= 0 ? 0 : (rem < BLK ? (int)rem : BLK);
+  const int64_t row0 = (c.tok0 + (int64_t)(b > 0 ? blk : 0) * BLK) * c.H + c.h;
+  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
+  const uint32_t valid = (uint32_t)b * rowbytes;
+  const auto rq = rsrc(c.q + row0 * D, valid);
+  const auto rk = rsrc(c.k + row0 * D, valid);
+  const auto rv = rsrc(c.v + row0 * D + c.c0, valid);
   const int ch = tid % C::CHUNKS, r0 = tid / C::CHUNKS;
 #pragma unroll
   for (int a = 0; a < C::QK_LOADS; ++a) {
-    const int row = r0 + a * C::ROWS_PER_LOAD;
-    if (row < b) {
-      const int64_t off = ((tok + row) * H + h) * (int64_t)D + 8 * ch;
-      r.q[a] = *(const uint4 *)(q + off);
-      r.k[a] = *(const uint4 *)(k + off);
-    } else {
-      r.q[a] = make_uint4(0, 0, 0, 0);
-      r.k[a] = make_uint4(0, 0, 0, 0);
-    }
+    const uint32_t off = (uint32_t)(r0 + a * C::ROWS_PER_LOAD) * rowbytes + 16u * ch;
+    r.q[a] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    r.k[a] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
   }
   const int vr = tid / (CV / 8), vc = tid % (CV / 8);
-  if (vr < b) {
-    r.v = *(const uint4 *)(v + ((tok + vr) * H + h) * (int64_t)D + c0 + 8 * vc);
-  } else {
-    r.v = make_uint4(0, 0, 0, 0);
-  }
+  r.v = __builtin_amdgcn_raw_buffer_load_b128(rv, (uint32_t)vr * rowbytes + 16u * vc, 0, 0);
 }
 
 template <int D>
@@ -126,11 +156,221 @@ __device__ __forceinline__ void store_block(const Regs<D> &r, __bf16 *stage, int
 #pragma unroll
   for (int a = 0; a < C::QK_LOADS; ++a) {
     const int row = r0 + a * C::ROWS_PER_LOAD;
-    *(uint4 *)(Qs + row * C::QROW + 8 * ch) = r.q[a];
-    *(uint4 *)(Ks + row * C::QROW + 8 * ch) = r.k[a];
+    *(u32x4 *)(Qs + row * C::QROW + 8 * ch) = r.q[a];
+    *(u32x4 *)(Ks + row * C::QROW + 8 * ch) = r.k[a];
   }
   const int vr = tid / (CV / 8), vc = tid % (CV / 8);
-  *(uint4 *)(Vs + vr * C::VROW + 8 * vc) = r.v;
+  *(u32x4 *)(Vs + vr * C::VROW + 8 * vc) = r.v;
+}
+
+// The block loop of wave W.
+template <int D, int W>
+__device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const float *pw,
+                                          const float *s0, float *fs, size_t sbase, int tid) {
+  using C = Cfg<D>;
+  using O = Own<D, W>;
+  constexpr int RT = O::RT;
+  constexpr int DK0 = O::DK0;
+  constexpr int NT = W + 1;  // causal score tiles of this wave
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int jrow = 16 * W + l16;  // this lane's output row inside a block
+
+  // fp32 state rows owned by this wave, as MFMA accumulators:
+  // kv[rt][ct][i] = KV[DK0 + 16 rt + 4 g + i][c0 + 16 ct + l16].
+  f32x4 kv[RT > 0 ? RT : 1][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
+        kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
+      }
+  __bf16 *const kvx0 = smem + 2 * C::STAGE;
+  auto write_kvx = [&](__bf16 *dst) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        *(bf16x4 *)(dst + (16 * ct + l16) * C::QROW + DK0 + 16 * rt + 4 * g) =
+            to_bf16x4(kv[rt][ct]);
+  };
+  write_kvx(kvx0);
+
+  Regs<D> ra, rb;
+  load_block<D>(ra, c, 0, tid);
+  store_block<D>(ra, smem, tid);
+  load_block<D>(rb, c, 1, tid);
+  __syncthreads();  // stage 0, state copy and pw visible
+
+  // Per-lane constants (the same for every full block).
+  float maskw[NT][4];  // lambda^(jrow - j'), j' = 16 t + 4 g + i, for j' <= jrow
+  bool keep[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jp = 16 * t + 4 * g + i;
+      keep[t][i] = jp <= jrow;
+      maskw[t][i] = keep[t][i] ? pw[jrow - jp] : 0.f;
+    }
+  const float inter_scale = pw[jrow + 1];
+  // Token of element e of this lane's 32-token k-step s: 32 s + 4 g + e (e < 4) and
+  // 32 s + 16 + 4 g + (e - 4) (e >= 4); lambda^(BLK-1-tok) for a full block.
+  float ksc_full[2][8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = 32 * s + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+      ksc_full[s][e] = pw[BLK - 1 - tok];
+    }
+  const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
+  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
+
+  auto step = [&](int i, Regs<D> &issue, Regs<D> &pending) {
+    const int cur = i & 1;
+    const int64_t rem = c.n - (int64_t)i * BLK;
+    const int b = rem < BLK ? (int)rem : BLK;
+    load_block<D>(issue, c, i + 2, tid);  // zero-filled past the end of the sequence
+    const __bf16 *Qs = smem + cur * C::STAGE;
+    const __bf16 *Ks = Qs + C::STAGE_QK;
+    const __bf16 *Vs = Ks + C::STAGE_QK;
+    const __bf16 *KVs = kvx0 + cur * C::KVX;
+
+    // Q operand (B of S^T and of the inter product): Q[jrow][32 ks + 8 g + 0..7].
+    bf16x8 qop[C::KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+      qop[ks] = *(const bf16x8 *)(Qs + jrow * C::QROW + 32 * ks + 8 * g);
+
+    // Intra scores, causal tiles only: S^T[16t + 4g + i][jrow] -> P[jrow][16t + 4g + i].
+    f32x4 sacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        sacc[t] = mfma(*(const bf16x8 *)(Ks + (16 * t + l16) * C::QROW + 32 * ks + 8 * g),
+                       qop[ks], sacc[t]);
+
+    // Inter part: O^T[16ct + 4g + i][jrow] = sum_dk KV[dk][16ct + 4g + i] Q[jrow][dk].
+    f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        o[ct] = mfma(*(const bf16x8 *)(KVs + (16 * ct + l16) * C::QROW + 32 * ks + 8 * g),
+                     qop[ks], o[ct]);
+
+    // V operands, token-major: vop[s][ct] lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
+    bf16x8 vop[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROW + 16 * ct + tcol);
+        const bf16x4 hi = tr_read(Vs + (32 * s + 16 + trow) * C::VROW + 16 * ct + tcol);
+        vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+
+    // Decay/causal mask in registers (select), then P in bf16.
+    bf16x4 p[2 * ((NT + 1) / 2)];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f32x4 m;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[e] = keep[t][e] ? sacc[t][e] * maskw[t][e] : 0.f;
+      p[t] = to_bf16x4(m);
+    }
+    if constexpr (NT % 2) p[NT] = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+
+    // O^T = lambda^(j+1) * inter + V^T P^T over the causal k-steps.
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) o[ct] *= inter_scale;
+#pragma unroll
+    for (int s = 0; s < (NT + 1) / 2; ++s) {
+      const bf16x8 pop = __builtin_shufflevector(p[2 * s], p[2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) o[ct] = mfma(vop[s][ct], pop, o[ct]);
+    }
+
+    // Store: lane holds O[jrow][c0 + 16ct + 4g + 0..3]; rows past the end are dropped.
+    {
+      const int64_t row0 = (c.tok0 + (int64_t)i * BLK) * c.H + c.h;
+      const auto ro = rsrc(c.out + row0 * D + c.c0, (uint32_t)b * rowbytes);
+      const uint32_t off = (uint32_t)jrow * rowbytes + 8u * g;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(o[ct])), ro,
+                                              off + 32u * ct, 0, 0);
+    }
+
+    // State update: KV = lambda^b KV + K^T diag(lambda^(b-1-tok)) V.
+    if (RT > 0) {
+      float ksc[2][8];
+      if (b == BLK) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ksc[s][e] = ksc_full[s][e];
+      } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tok = 32 * s + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+            ksc[s][e] = tok < b ? pw[b - 1 - tok] : 0.f;
+          }
+      }
+      const float lb = pw[b];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) kv[rt][ct] *= lb;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int col = DK0 + 16 * rt + tcol;
+          const bf16x4 lo = tr_read(Ks + (32 * s + trow) * C::QROW + col);
+          const bf16x4 hi = tr_read(Ks + (32 * s + 16 + trow) * C::QROW + col);
+          bf16x8 kop;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kop[e] = (__bf16)((float)lo[e] * ksc[s][e]);
+            kop[e + 4] = (__bf16)((float)hi[e] * ksc[s][e + 4]);
+          }
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) kv[rt][ct] = mfma(kop, vop[s][ct], kv[rt][ct]);
+        }
+      }
+    }
+
+    // Publish the new state (bf16) for the next block's inter product; stage block i+1.
+    write_kvx(kvx0 + (cur ^ 1) * C::KVX);
+    store_block<D>(pending, smem + (cur ^ 1) * C::STAGE, tid);
+    __syncthreads();
+  };
+
+  for (int i = 0; i < c.nb; i += 2) {
+    step(i, ra, rb);
+    if (i + 1 < c.nb) step(i + 1, rb, ra);
+  }
+
+  if (fs) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
+          fs[sbase + (size_t)dk * D + dv] = kv[rt][ct][i];
+        }
+  }
 }
 
 template <int D>
@@ -157,218 +397,32 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     slice = wg % NS;
   }
   const int seq = chain / H, h = chain % H;
-  const int64_t tok0 = cu ? (int64_t)cu[seq] : 0;
+  Chain c;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.out = out;
+  c.tok0 = cu ? (int64_t)cu[seq] : 0;
   const int64_t tok1 = cu ? (int64_t)cu[seq + 1] : T;
-  const int64_t n = tok1 > tok0 ? tok1 - tok0 : 0;
-  const int nb = (int)((n + BLK - 1) / BLK);
-  const int c0 = slice * CV;
+  c.n = tok1 > c.tok0 ? tok1 - c.tok0 : 0;
+  c.nb = (int)((c.n + BLK - 1) / BLK);
+  c.H = H;
+  c.h = h;
+  c.c0 = slice * CV;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const float lam = decay[h];
-
+  const int tid = threadIdx.x;
   if (tid <= BLK) {
+    const float lam = decay[h];
     double p = 1.0;  // lambda^tid by repeated multiplication (0^0 = 1)
     for (int i = 0; i < tid; ++i) p *= (double)lam;
     pw[tid] = (float)p;
   }
-
-  // fp32 state rows owned by this wave, as MFMA accumulators: kv[rt][ct][i] =
-  // KV[dk0 + 16 rt + 4 g + i][c0 + 16 ct + l16].
-  const int dk0 = w * (D / 4);
-  f32x4 kv[C::RT][2];
   const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
-#pragma unroll
-  for (int rt = 0; rt < C::RT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dk = dk0 + 16 * rt + 4 * g + i, dv = c0 + 16 * ct + l16;
-        kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
-      }
-
-  __bf16 *const kvx0 = smem + 2 * C::STAGE;
-  auto write_kvx = [&](__bf16 *dst) {
-#pragma unroll
-    for (int rt = 0; rt < C::RT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        *(bf16x4 *)(dst + (16 * ct + l16) * C::QROW + dk0 + 16 * rt + 4 * g) =
-            to_bf16x4(kv[rt][ct]);
-  };
-  write_kvx(kvx0);
-
-  Regs<D> ra, rb;
-  if (nb > 0) {
-    load_block<D>(ra, q, k, v, tok0, (int)(n < BLK ? n : BLK), H, h, c0, tid);
-    store_block<D>(ra, smem, tid);
-  }
-  if (nb > 1) load_block<D>(rb, q, k, v, tok0 + BLK, (int)(n - BLK < BLK ? n - BLK : BLK), H, h,
-                            c0, tid);
-  __syncthreads();
-
-  // Per-lane constants (the same for every full block).
-  const int jrow = 16 * w + l16;  // this lane's output row inside a block
-  float maskw[4][4];              // lambda^(jrow - j'), j' = 16 t + 4 g + i
-  bool keep[4][4];                // j' <= jrow
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jp = 16 * t + 4 * g + i;
-      keep[t][i] = jp <= jrow;
-      maskw[t][i] = keep[t][i] ? pw[jrow - jp] : 0.f;
-    }
-  const float inter_scale = pw[jrow + 1];
-  // lambda^(BLK-1-tok) for the 8 tokens of each 32-token k-step held by this lane:
-  // tok = 32 s + 4 g + e (e < 4) and 32 s + 16 + 4 g + (e - 4) (e >= 4).
-  float ksc_full[2][8];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = 32 * s + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-      ksc_full[s][e] = pw[BLK - 1 - tok];
-    }
-
-  auto step = [&](int i, Regs<D> &issue, Regs<D> &pending) {
-    const int cur = i & 1;
-    const int64_t btok = tok0 + (int64_t)i * BLK;
-    const int b = (int)(n - (int64_t)i * BLK < BLK ? n - (int64_t)i * BLK : BLK);
-    if (i + 2 < nb) {
-      const int64_t rem = n - (int64_t)(i + 2) * BLK;
-      load_block<D>(issue, q, k, v, btok + 2 * BLK, (int)(rem < BLK ? rem : BLK), H, h, c0, tid);
-    }
-    const __bf16 *Qs = smem + cur * C::STAGE;
-    const __bf16 *Ks = Qs + C::STAGE_QK;
-    const __bf16 *Vs = Ks + C::STAGE_QK;
-    const __bf16 *KVs = kvx0 + cur * C::KVX;
-
-    // Q operand (B of S^T and of the inter product): Q[jrow][32 ks + 8 g + 0..7].
-    bf16x8 qop[C::KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks)
-      qop[ks] = *(const bf16x8 *)(Qs + jrow * C::QROW + 32 * ks + 8 * g);
-
-    // Intra scores, causal tiles only: S^T[16t + 4g + i][jrow] -> P[jrow][16t + 4g + i].
-    bf16x4 p[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t <= w) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks)
-          acc = mfma(*(const bf16x8 *)(Ks + (16 * t + l16) * C::QROW + 32 * ks + 8 * g), qop[ks],
-                     acc);
-        f32x4 m;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m[e] = keep[t][e] ? acc[e] * maskw[t][e] : 0.f;
-        p[t] = to_bf16x4(m);
-      } else {
-        p[t] = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-      }
-    }
-
-    // Inter part: O^T[16ct + 4g + i][jrow] = sum_dk KV[dk][16ct + 4g + i] Q[jrow][dk].
-    f32x4 o[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks)
-        o[ct] = mfma(*(const bf16x8 *)(KVs + (16 * ct + l16) * C::QROW + 32 * ks + 8 * g),
-                     qop[ks], o[ct]);
-      o[ct] *= inter_scale;
-    }
-
-    // V operands, token-major: vop[s][ct] lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
-    bf16x8 vop[2][2];
-    const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROW + 16 * ct + tcol);
-        const bf16x4 hi = tr_read(Vs + (32 * s + 16 + trow) * C::VROW + 16 * ct + tcol);
-        vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-
-    // Intra part: O^T += V^T P^T over the causal k-steps.
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (2 * s <= w) {
-        const bf16x8 pop = __builtin_shufflevector(p[2 * s], p[2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) o[ct] = mfma(vop[s][ct], pop, o[ct]);
-      }
-    }
-
-    // Store: lane holds O[jrow][c0 + 16ct + 4g + 0..3].
-    if (jrow < b) {
-      __bf16 *op = out + ((btok + jrow) * H + h) * (int64_t)D + c0 + 4 * g;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) *(bf16x4 *)(op + 16 * ct) = to_bf16x4(o[ct]);
-    }
-
-    // State update: KV = lambda^b KV + K^T diag(lambda^(b-1-tok)) V.
-    float ksc[2][8];
-    if (b == BLK) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ksc[s][e] = ksc_full[s][e];
-    } else {
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = 32 * s + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-          ksc[s][e] = tok < b ? pw[b - 1 - tok] : 0.f;
-        }
-    }
-    const float lb = pw[b];
-#pragma unroll
-    for (int rt = 0; rt < C::RT; ++rt) {
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) kv[rt][ct] *= lb;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int col = dk0 + 16 * rt + tcol;
-        const bf16x4 lo = tr_read(Ks + (32 * s + trow) * C::QROW + col);
-        const bf16x4 hi = tr_read(Ks + (32 * s + 16 + trow) * C::QROW + col);
-        bf16x8 kop;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kop[e] = (__bf16)((float)lo[e] * ksc[s][e]);
-          kop[e + 4] = (__bf16)((float)hi[e] * ksc[s][e + 4]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) kv[rt][ct] = mfma(kop, vop[s][ct], kv[rt][ct]);
-      }
-    }
-
-    // Publish the new state (bf16) for the next block's inter product; stage block i+1.
-    write_kvx(kvx0 + (cur ^ 1) * C::KVX);
-    if (i + 1 < nb) store_block<D>(pending, smem + (cur ^ 1) * C::STAGE, tid);
-    __syncthreads();
-  };
-
-  for (int i = 0; i < nb; i += 2) {
-    step(i, ra, rb);
-    if (i + 1 < nb) step(i + 1, rb, ra);
-  }
-
-  if (fs) {
-#pragma unroll
-    for (int rt = 0; rt < C::RT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int dk = dk0 + 16 * rt + 4 * g + i, dv = c0 + 16 * ct + l16;
-          fs[sbase + (size_t)dk * D + dv] = kv[rt][ct][i];
-        }
+  switch (tid >> 6) {
+    case 0: wave_loop<D, 0>(c, smem, pw, s0, fs, sbase, tid); break;
+    case 1: wave_loop<D, 1>(c, smem, pw, s0, fs, sbase, tid); break;
+    case 2: wave_loop<D, 2>(c, smem, pw, s0, fs, sbase, tid); break;
+    default: wave_loop<D, 3>(c, smem, pw, s0, fs, sbase, tid); break;
   }
 }
 
