@@ -2,8 +2,8 @@
 
 Usage:  python -m long_context_attention_attn_amd.build
 Each .hip file is compiled to an object in parallel, then linked into one shared library next
-to this file.  Flags: -O3, code-object v5, and packed-fp32 instructions disabled
-(-Xclang -target-feature -Xclang -packed-fp32-ops).
+to this file.  Flags: -O3, code-object v5, packed-fp32 instructions disabled
+(-Xclang -target-feature -Xclang -packed-fp32-ops), MFMA accumulators in VGPRs.
 """
 from __future__ import annotations
 
@@ -26,6 +26,9 @@ COMMON = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-result",
+    # keep MFMA accumulators in ordinary VGPRs (no AGPR<->VGPR copies around the VALU work
+    # that reads them)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

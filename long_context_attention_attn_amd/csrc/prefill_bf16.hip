@@ -55,17 +55,21 @@ constexpr int RSRC_WORD3 = 0x00020000;  // buffer descriptor dword 3 for raw 32-
 
 template <int D>
 struct Cfg {
-  static constexpr int QROW = D + PAD;                    // LDS row stride of Q, K (elements)
-  static constexpr int VROW = CV + PAD;                   // LDS row stride of V
-  static constexpr int CHUNKS = D / 8;                    // 16-byte chunks per Q/K row
-  static constexpr int QK_LOADS = BLK * CHUNKS / NTHR;    // chunks per thread per tensor
-  static constexpr int ROWS_PER_LOAD = NTHR / CHUNKS;
-  static constexpr int KSTEPS = D / 32;                   // MFMA k-steps over features
-  static constexpr int STAGE_QK = BLK * QROW;
-  static constexpr int STAGE_V = BLK * VROW;
-  static constexpr int STAGE = 2 * STAGE_QK + STAGE_V;    // Q, K, V of one block
-  static constexpr int KVX = CV * QROW;                   // bf16 state copy, [CV][D] (+pad)
-  static constexpr int SMEM = 2 * STAGE + 2 * KVX;
+  static constexpr int ROWB = 2 * D;                       // bytes per Q/K row in LDS
+  static constexpr int CH = D / 8;                         // 16-byte chunks per Q/K row
+  static constexpr int RPI = 1024 / ROWB;                  // rows per 1 KiB DMA instruction
+  static constexpr int QK_DMA = 16 / RPI;                  // DMA instructions per wave (16 rows)
+  static constexpr int KSTEPS = D / 32;                    // MFMA k-steps over features
+  static constexpr int VROWB = 2 * CV;                     // bytes per V row
+  static constexpr int Q_OFF = 0;                          // byte offsets inside a stage
+  static constexpr int K_OFF = BLK * ROWB;
+  static constexpr int V_OFF = 2 * BLK * ROWB;
+  static constexpr int STAGE = 2 * BLK * ROWB + BLK * VROWB;
+  static constexpr int NST = 3;                            // pipeline stages (blocks in LDS)
+  static constexpr int KVX = CV * ROWB;                    // bf16 state copy [CV][D]
+  static constexpr int KVX_OFF = NST * STAGE;
+  static constexpr int SMEM = NST * STAGE + 2 * KVX;
+  static constexpr int VMEM_PER_STEP = 2 * QK_DMA + 1 + 2; // DMA + output stores per wave
 };
 
 // State rows (16-row tiles) owned by wave W, and the first owned row.  Low waves do fewer
@@ -78,13 +82,6 @@ struct Own {
   static constexpr int first(int w) { return w == 0 ? 0 : first(w - 1) + 16 * tiles(w - 1); }
   static constexpr int RT = tiles(W);
   static constexpr int DK0 = first(W);
-};
-
-template <int D>
-struct Regs {
-  u32x4 q[Cfg<D>::QK_LOADS];
-  u32x4 k[Cfg<D>::QK_LOADS];
-  u32x4 v;
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -105,13 +102,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
                                            RSRC_WORD3);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
+// lds_base + 16 l (lds_base wave-uniform).  Written as inline assembly so that the compiler
+// does not track it; completion is waited for explicitly (vmcnt) before the barrier that
+// publishes a stage.  Out-of-range offsets (buffer range check) read as zero.
+// M0 (which holds the LDS address) is saved and restored around the copy; the s_nop covers the
+// one wait state required between an M0 write and an LDS DMA that reads it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(r)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding and all its LDS
+// operations are done, then barrier.  A compiler barrier for memory operations too.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)(p);
+}
+
 // Transpose read: within each 16-lane group, lane c receives element c of the four 4-element
 // pieces addressed by lanes 4e + c/4 (e = 0..3).  With lane s pointing at row base + s/4,
 // column col0 + 4*(s%4) of a row-major tile, lane c receives rows base..base+3 of column
 // col0 + c.
-__device__ __forceinline__ bf16x4 tr_read(const __bf16 *p) {
+__device__ __forceinline__ bf16x4 tr_read(const char *p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
   return __builtin_bit_cast(bf16x4, r);
+}
+
+// Byte offset of (row, element col) in a swizzled [rows][D] bf16 tile: 16-byte chunk c of row
+// r is stored at chunk position c ^ (r % CH), so 16 lanes reading one chunk column of 16
+// consecutive rows hit 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  using C = Cfg<D>;
+  return row * C::ROWB + ((((col >> 3) ^ row) & (C::CH - 1)) << 4) + ((col & 7) << 1);
 }
 
 // Everything a wave needs about its workgroup's chain.
@@ -124,10 +160,11 @@ struct Chain {
   int H, h, c0;  // heads, this head, first value column of the slice
 };
 
-// Fetch block `blk` of the chain into registers.  Rows at or past the end of the sequence
-// (and whole blocks past the end) read as zero through buffer range checking.
+// Issue this wave's share of the DMA of block `blk` into `stage`: its 16 Q rows, 16 K rows and
+// 16 V rows (rows 16w..16w+15).  Rows past the end of the sequence (and whole blocks past the
+// end) read as zero through the buffer range check.
 template <int D>
-__device__ __forceinline__ void load_block(Regs<D> &r, const Chain &c, int blk, int tid) {
+__device__ __forceinline__ void dma_block(const Chain &c, int blk, char *stage, int w, int lane) {
   using C = Cfg<D>;
   const int64_t rem = c.n - (int64_t)blk * BLK;
   const int b = rem <= 0 ? 0 : (rem < BLK ? (int)rem : BLK);
@@ -137,41 +174,30 @@ __device__ __forceinline__ void load_block(Regs<D> &r, const Chain &c, int blk, 
   const auto rq = rsrc(c.q + row0 * D, valid);
   const auto rk = rsrc(c.k + row0 * D, valid);
   const auto rv = rsrc(c.v + row0 * D + c.c0, valid);
-  const int ch = tid % C::CHUNKS, r0 = tid / C::CHUNKS;
+  const uint32_t sbase = lds_addr(stage);
 #pragma unroll
-  for (int a = 0; a < C::QK_LOADS; ++a) {
-    const uint32_t off = (uint32_t)(r0 + a * C::ROWS_PER_LOAD) * rowbytes + 16u * ch;
-    r.q[a] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-    r.k[a] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+  for (int a = 0; a < C::QK_DMA; ++a) {
+    const int row = 16 * w + a * C::RPI + lane / C::CH;
+    const int chunk = (lane % C::CH) ^ (row % C::CH);
+    const uint32_t off = (uint32_t)row * rowbytes + 16u * chunk;
+    const uint32_t dst = (uint32_t)((16 * w + a * C::RPI) * C::ROWB);
+    dma16(rq, off, sbase + C::Q_OFF + dst);
+    dma16(rk, off, sbase + C::K_OFF + dst);
   }
-  const int vr = tid / (CV / 8), vc = tid % (CV / 8);
-  r.v = __builtin_amdgcn_raw_buffer_load_b128(rv, (uint32_t)vr * rowbytes + 16u * vc, 0, 0);
-}
-
-template <int D>
-__device__ __forceinline__ void store_block(const Regs<D> &r, __bf16 *stage, int tid) {
-  using C = Cfg<D>;
-  __bf16 *Qs = stage, *Ks = stage + C::STAGE_QK, *Vs = stage + 2 * C::STAGE_QK;
-  const int ch = tid % C::CHUNKS, r0 = tid / C::CHUNKS;
-#pragma unroll
-  for (int a = 0; a < C::QK_LOADS; ++a) {
-    const int row = r0 + a * C::ROWS_PER_LOAD;
-    *(u32x4 *)(Qs + row * C::QROW + 8 * ch) = r.q[a];
-    *(u32x4 *)(Ks + row * C::QROW + 8 * ch) = r.k[a];
-  }
-  const int vr = tid / (CV / 8), vc = tid % (CV / 8);
-  *(u32x4 *)(Vs + vr * C::VROW + 8 * vc) = r.v;
+  const int vrow = 16 * w + lane / 4;
+  dma16(rv, (uint32_t)vrow * rowbytes + 16u * (lane % 4), sbase + C::V_OFF + 16 * w * C::VROWB);
 }
 
 // The block loop of wave W.
 template <int D, int W>
-__device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const float *pw,
+__device__ __forceinline__ void wave_loop(const Chain &c, char *smem, const float *pw,
                                           const float *s0, float *fs, size_t sbase, int tid) {
   using C = Cfg<D>;
   using O = Own<D, W>;
   constexpr int RT = O::RT;
   constexpr int DK0 = O::DK0;
   constexpr int NT = W + 1;  // causal score tiles of this wave
+  constexpr int NST = C::NST;
   const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int jrow = 16 * W + l16;  // this lane's output row inside a block
 
@@ -187,22 +213,15 @@ __device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const fl
         const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
         kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
       }
-  __bf16 *const kvx0 = smem + 2 * C::STAGE;
-  auto write_kvx = [&](__bf16 *dst) {
+  char *const kvx0 = smem + C::KVX_OFF;
+  auto write_kvx = [&](char *dst) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        *(bf16x4 *)(dst + (16 * ct + l16) * C::QROW + DK0 + 16 * rt + 4 * g) =
-            to_bf16x4(kv[rt][ct]);
+        *(bf16x4 *)(dst + swz<D>(16 * ct + l16, DK0 + 16 * rt + 4 * g)) = to_bf16x4(kv[rt][ct]);
   };
   write_kvx(kvx0);
-
-  Regs<D> ra, rb;
-  load_block<D>(ra, c, 0, tid);
-  store_block<D>(ra, smem, tid);
-  load_block<D>(rb, c, 1, tid);
-  __syncthreads();  // stage 0, state copy and pw visible
 
   // Per-lane constants (the same for every full block).
   float maskw[NT][4];  // lambda^(jrow - j'), j' = 16 t + 4 g + i, for j' <= jrow
@@ -229,21 +248,27 @@ __device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const fl
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
   const uint32_t rowbytes = (uint32_t)c.H * D * 2;
 
-  auto step = [&](int i, Regs<D> &issue, Regs<D> &pending) {
-    const int cur = i & 1;
+  // Prologue: blocks 0 .. NST-2 in flight; wait for block 0.
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) dma_block<D>(c, s, smem + s * C::STAGE, W, lane);
+  wait_vm_barrier<(NST - 2) * (2 * C::QK_DMA + 1)>();
+
+  for (int i = 0; i < c.nb; ++i) {
+    const int cur = i % NST;
     const int64_t rem = c.n - (int64_t)i * BLK;
     const int b = rem < BLK ? (int)rem : BLK;
-    load_block<D>(issue, c, i + 2, tid);  // zero-filled past the end of the sequence
-    const __bf16 *Qs = smem + cur * C::STAGE;
-    const __bf16 *Ks = Qs + C::STAGE_QK;
-    const __bf16 *Vs = Ks + C::STAGE_QK;
-    const __bf16 *KVs = kvx0 + cur * C::KVX;
+    // Refill the stage consumed in step i-1 (every wave has passed the barrier since).
+    dma_block<D>(c, i + NST - 1, smem + ((i + NST - 1) % NST) * C::STAGE, W, lane);
+    const char *Qs = smem + cur * C::STAGE + C::Q_OFF;
+    const char *Ks = smem + cur * C::STAGE + C::K_OFF;
+    const char *Vs = smem + cur * C::STAGE + C::V_OFF;
+    const char *KVs = kvx0 + (i & 1) * C::KVX;
 
     // Q operand (B of S^T and of the inter product): Q[jrow][32 ks + 8 g + 0..7].
     bf16x8 qop[C::KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks)
-      qop[ks] = *(const bf16x8 *)(Qs + jrow * C::QROW + 32 * ks + 8 * g);
+      qop[ks] = *(const bf16x8 *)(Qs + swz<D>(jrow, 32 * ks + 8 * g));
 
     // Intra scores, causal tiles only: S^T[16t + 4g + i][jrow] -> P[jrow][16t + 4g + i].
     f32x4 sacc[NT];
@@ -253,8 +278,8 @@ __device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const fl
     for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        sacc[t] = mfma(*(const bf16x8 *)(Ks + (16 * t + l16) * C::QROW + 32 * ks + 8 * g),
-                       qop[ks], sacc[t]);
+        sacc[t] = mfma(*(const bf16x8 *)(Ks + swz<D>(16 * t + l16, 32 * ks + 8 * g)), qop[ks],
+                       sacc[t]);
 
     // Inter part: O^T[16ct + 4g + i][jrow] = sum_dk KV[dk][16ct + 4g + i] Q[jrow][dk].
     f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -262,8 +287,8 @@ __device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const fl
     for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        o[ct] = mfma(*(const bf16x8 *)(KVs + (16 * ct + l16) * C::QROW + 32 * ks + 8 * g),
-                     qop[ks], o[ct]);
+        o[ct] = mfma(*(const bf16x8 *)(KVs + swz<D>(16 * ct + l16, 32 * ks + 8 * g)), qop[ks],
+                     o[ct]);
 
     // V operands, token-major: vop[s][ct] lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
     bf16x8 vop[2][2];
@@ -271,8 +296,8 @@ __device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const fl
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROW + 16 * ct + tcol);
-        const bf16x4 hi = tr_read(Vs + (32 * s + 16 + trow) * C::VROW + 16 * ct + tcol);
+        const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROWB + 2 * (16 * ct + tcol));
+        const bf16x4 hi = tr_read(Vs + (32 * s + 16 + trow) * C::VROWB + 2 * (16 * ct + tcol));
         vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 
@@ -335,8 +360,8 @@ __device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const fl
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int col = DK0 + 16 * rt + tcol;
-          const bf16x4 lo = tr_read(Ks + (32 * s + trow) * C::QROW + col);
-          const bf16x4 hi = tr_read(Ks + (32 * s + 16 + trow) * C::QROW + col);
+          const bf16x4 lo = tr_read(Ks + swz<D>(32 * s + trow, col));
+          const bf16x4 hi = tr_read(Ks + swz<D>(32 * s + 16 + trow, col));
           bf16x8 kop;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -349,16 +374,21 @@ __device__ __forceinline__ void wave_loop(const Chain &c, __bf16 *smem, const fl
       }
     }
 
-    // Publish the new state (bf16) for the next block's inter product; stage block i+1.
-    write_kvx(kvx0 + (cur ^ 1) * C::KVX);
-    store_block<D>(pending, smem + (cur ^ 1) * C::STAGE, tid);
-    __syncthreads();
-  };
-
-  for (int i = 0; i < c.nb; i += 2) {
-    step(i, ra, rb);
-    if (i + 1 < c.nb) step(i + 1, rb, ra);
+    // Publish the new state (bf16) for the next block's inter product; wait until block i+1
+    // has landed in LDS (its DMA was issued NST-2 steps ago, or in the prologue).
+    write_kvx(kvx0 + ((i + 1) & 1) * C::KVX);
+    constexpr int DMA = 2 * C::QK_DMA + 1;
+    constexpr int PER = C::VMEM_PER_STEP;
+    if (NST == 3) {
+      if (i == 0) wait_vm_barrier<PER>();
+      else wait_vm_barrier<2 + PER>();
+    } else {
+      static_assert(NST == 3, "wait counts are written for three stages");
+      wait_vm_barrier<DMA>();
+    }
   }
+  // Drain the DMAs still in flight (they target this workgroup's LDS) before leaving.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (fs) {
 #pragma unroll
@@ -381,7 +411,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     int S, int H) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[C::SMEM];
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   __shared__ float pw[BLK + 1];  // lambda^m, m = 0..BLK
 
   // Workgroup -> (chain = sequence*H + head, value slice); slices of a chain share an XCD.
@@ -417,6 +447,11 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     for (int i = 0; i < tid; ++i) p *= (double)lam;
     pw[tid] = (float)p;
   }
+  // Zero the stages once: rows a partial block does not load then hold zeros or finite values
+  // of earlier blocks, never stale bits from another kernel.
+  for (int off = 16 * tid; off < C::NST * C::STAGE; off += 16 * NTHR)
+    *(u32x4 *)(smem + off) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();  // pw and zeroed stages visible before any DMA or read
   const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   switch (tid >> 6) {
     case 0: wave_loop<D, 0>(c, smem, pw, s0, fs, sbase, tid); break;
