@@ -17,20 +17,25 @@
 //     columns are independent: KV[:, c] and O[:, c] depend on V[:, c] only.  The D/32 slices
 //     of one head read the same Q and K blocks, so the workgroup index is mapped so that they
 //     land on the same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
-//   * 4 waves, one per SIMD.  Wave w owns output rows 16w..16w+15 of each block; its causal
-//     score work grows with w (w+1 score tiles), so the fp32 state rows, held in MFMA
-//     accumulators for the whole sequence, are dealt unevenly (more to the low waves) to even
-//     out the MFMA count per wave.  Each wave's role is a template parameter, so every loop
-//     trip count is static and the code between barriers is straight-line.
-//   * per block and wave: S^T = K Q^T tiles, decay mask applied in registers; the S^T
-//     accumulator layout is exactly the B-operand layout of P for O^T += V^T P^T, so P never
-//     leaves registers.  O^T = KV^T Q^T (inter) reads a bf16 copy of the previous state shared
-//     through LDS.  The state update K^T (Lambda V) reads K and V token-major through
-//     ds_read_b64_tr_b16 (LDS transpose reads), so tiles are staged once, row-major.
-//   * q/k/v blocks are fetched with buffer loads two blocks ahead into registers and written
-//     to a double-buffered LDS stage; one barrier per block.  Buffer range checking zero-fills
-//     rows past the end of a sequence and drops stores past it, so there are no branches
-//     around memory operations (which lets the compiler wait on exactly the loads it needs).
+//   * 8 waves, two per SIMD, in two specialised roles that run side by side on each SIMD so
+//     that one wave's VALU work overlaps the other's MFMA and LDS traffic:
+//       - output wave r (r = 0..3) owns output rows 16r..16r+15 of each block: S^T = K Q^T on
+//         its r+1 causal tiles, decay mask in registers, O^T = lambda^(j+1) KV^T Q^T + V^T P^T
+//         (the S^T accumulator layout is exactly the B-operand layout of P, so P never leaves
+//         registers), and the store;
+//       - state wave r owns a band of rows of the fp32 state, kept in MFMA accumulators for
+//         the whole sequence: KV = lambda^b KV + K^T diag(lambda^(b-1-j)) V, reading K and the
+//         decayed copy diag(lambda^(b-1-j)) V token-major through ds_read_b64_tr_b16 (LDS
+//         transpose reads), then publishes a bf16 copy of its rows for the next block's inter
+//         product.  Bands are dealt unevenly so that each SIMD's pair of waves carries about
+//         the same MFMA work.  The decayed V copy is written once per block by the output
+//         waves (each scales the 16 V rows it loads), so no state wave scales operands.
+//     Every role is a template instance, so trip counts are static and code between
+//     barriers is straight-line.
+//   * q/k/v blocks go straight from HBM into LDS (buffer_load ... lds), two blocks ahead of
+//     the one being computed, in a three-stage ring with explicit waits; one barrier per
+//     block.  Buffer range checking zero-fills rows past the end of a sequence and drops
+//     stores past it, so there are no branches around memory operations.
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l (g = l/16, c = l%16) holds A[c][k in K(g)],
 // B[k in K(g)][c] and C[4g+i][c], i = 0..3; any k-assignment K(g) shared by A and B gives
@@ -49,8 +54,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BLK = 64;   // tokens per block
 constexpr int CV = 32;    // value columns per workgroup
-constexpr int NTHR = 256; // 4 waves
-constexpr int PAD = 8;    // bf16 padding per LDS row (keeps 16-byte alignment, spreads banks)
+constexpr int NTHR = 512; // 8 waves
+constexpr int NST = 3;    // pipeline stages (blocks resident in LDS)
 constexpr int RSRC_WORD3 = 0x00020000;  // buffer descriptor dword 3 for raw 32-bit accesses
 
 template <int D>
@@ -58,30 +63,31 @@ struct Cfg {
   static constexpr int ROWB = 2 * D;                       // bytes per Q/K row in LDS
   static constexpr int CH = D / 8;                         // 16-byte chunks per Q/K row
   static constexpr int RPI = 1024 / ROWB;                  // rows per 1 KiB DMA instruction
-  static constexpr int QK_DMA = 16 / RPI;                  // DMA instructions per wave (16 rows)
+  static constexpr int QK_DMA = 16 / RPI;                  // DMA instructions per 16 rows
   static constexpr int KSTEPS = D / 32;                    // MFMA k-steps over features
   static constexpr int VROWB = 2 * CV;                     // bytes per V row
   static constexpr int Q_OFF = 0;                          // byte offsets inside a stage
   static constexpr int K_OFF = BLK * ROWB;
   static constexpr int V_OFF = 2 * BLK * ROWB;
   static constexpr int STAGE = 2 * BLK * ROWB + BLK * VROWB;
-  static constexpr int NST = 3;                            // pipeline stages (blocks in LDS)
   static constexpr int KVX = CV * ROWB;                    // bf16 state copy [CV][D]
   static constexpr int KVX_OFF = NST * STAGE;
-  static constexpr int SMEM = NST * STAGE + 2 * KVX;
-  static constexpr int VMEM_PER_STEP = 2 * QK_DMA + 1 + 2; // DMA + output stores per wave
+  static constexpr int LV = BLK * VROWB;                   // decayed V copy, [BLK][CV]
+  static constexpr int LV_OFF = NST * STAGE + 2 * KVX;
+  static constexpr int SMEM = NST * STAGE + 2 * KVX + 2 * LV;
 };
 
-// State rows (16-row tiles) owned by wave W, and the first owned row.  Low waves do fewer
-// causal score tiles, so they take more state tiles.
-template <int D, int W>
-struct Own {
+// State rows owned by state wave R (in 16-row tiles) and its first row.  Output wave r does
+// r+1 score tiles, so the low bands are larger: each SIMD's pair then does about the same
+// number of MFMAs.
+template <int D, int R>
+struct Band {
   static constexpr int T128[4] = {3, 3, 1, 1};
   static constexpr int T64[4] = {2, 1, 1, 0};
-  static constexpr int tiles(int w) { return D == 128 ? T128[w] : T64[w]; }
-  static constexpr int first(int w) { return w == 0 ? 0 : first(w - 1) + 16 * tiles(w - 1); }
-  static constexpr int RT = tiles(W);
-  static constexpr int DK0 = first(W);
+  static constexpr int tiles(int r) { return D == 128 ? T128[r] : T64[r]; }
+  static constexpr int first(int r) { return r == 0 ? 0 : first(r - 1) + 16 * tiles(r - 1); }
+  static constexpr int RT = tiles(R);
+  static constexpr int DK0 = first(R);
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -97,6 +103,13 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   return r;
 }
 
+__device__ __forceinline__ bf16x8 scale8(bf16x8 x, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)((float)x[e] * s);
+  return r;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            RSRC_WORD3);
@@ -105,9 +118,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
 // lds_base + 16 l (lds_base wave-uniform).  Written as inline assembly so that the compiler
 // does not track it; completion is waited for explicitly (vmcnt) before the barrier that
-// publishes a stage.  Out-of-range offsets (buffer range check) read as zero.
-// M0 (which holds the LDS address) is saved and restored around the copy; the s_nop covers the
-// one wait state required between an M0 write and an LDS DMA that reads it.
+// publishes a stage.  Out-of-range offsets (buffer range check) read as zero.  M0 (the LDS
+// address) is saved and restored; the s_nop is the wait state an M0 write needs before an
+// LDS DMA reads it.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -122,10 +135,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding and all its LDS
-// operations are done, then barrier.  A compiler barrier for memory operations too.
+// operations are done, then barrier.  Also a compiler barrier for memory operations.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -160,109 +180,107 @@ struct Chain {
   int H, h, c0;  // heads, this head, first value column of the slice
 };
 
-// Issue this wave's share of the DMA of block `blk` into `stage`: its 16 Q rows, 16 K rows and
-// 16 V rows (rows 16w..16w+15).  Rows past the end of the sequence (and whole blocks past the
-// end) read as zero through the buffer range check.
-template <int D>
-__device__ __forceinline__ void dma_block(const Chain &c, int blk, char *stage, int w, int lane) {
-  using C = Cfg<D>;
+// Rows of block `blk` that exist (0 past the end) and the element offset of its first row.
+__device__ __forceinline__ int block_rows(const Chain &c, int blk, int64_t &row0) {
   const int64_t rem = c.n - (int64_t)blk * BLK;
   const int b = rem <= 0 ? 0 : (rem < BLK ? (int)rem : BLK);
-  const int64_t row0 = (c.tok0 + (int64_t)(b > 0 ? blk : 0) * BLK) * c.H + c.h;
-  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  const uint32_t valid = (uint32_t)b * rowbytes;
-  const auto rq = rsrc(c.q + row0 * D, valid);
-  const auto rk = rsrc(c.k + row0 * D, valid);
-  const auto rv = rsrc(c.v + row0 * D + c.c0, valid);
-  const uint32_t sbase = lds_addr(stage);
-#pragma unroll
-  for (int a = 0; a < C::QK_DMA; ++a) {
-    const int row = 16 * w + a * C::RPI + lane / C::CH;
-    const int chunk = (lane % C::CH) ^ (row % C::CH);
-    const uint32_t off = (uint32_t)row * rowbytes + 16u * chunk;
-    const uint32_t dst = (uint32_t)((16 * w + a * C::RPI) * C::ROWB);
-    dma16(rq, off, sbase + C::Q_OFF + dst);
-    dma16(rk, off, sbase + C::K_OFF + dst);
-  }
-  const int vrow = 16 * w + lane / 4;
-  dma16(rv, (uint32_t)vrow * rowbytes + 16u * (lane % 4), sbase + C::V_OFF + 16 * w * C::VROWB);
+  row0 = (c.tok0 + (int64_t)(b > 0 ? blk : 0) * BLK) * c.H + c.h;
+  return b;
 }
 
-// The block loop of wave W.
-template <int D, int W>
-__device__ __forceinline__ void wave_loop(const Chain &c, char *smem, const float *pw,
-                                          const float *s0, float *fs, size_t sbase, int tid) {
+// DMA 16 rows (16r..16r+15) of a [64][D] tile of block `blk` into its swizzled LDS image.
+template <int D>
+__device__ __forceinline__ void dma_rows(const __bf16 *base, const Chain &c, int blk, int r,
+                                         uint32_t lds_tile, int lane) {
   using C = Cfg<D>;
-  using O = Own<D, W>;
-  constexpr int RT = O::RT;
-  constexpr int DK0 = O::DK0;
-  constexpr int NT = W + 1;  // causal score tiles of this wave
-  constexpr int NST = C::NST;
-  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int jrow = 16 * W + l16;  // this lane's output row inside a block
+  int64_t row0;
+  const int b = block_rows(c, blk, row0);
+  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
+  const auto rs = rsrc(base + row0 * D, (uint32_t)b * rowbytes);
+#pragma unroll
+  for (int a = 0; a < C::QK_DMA; ++a) {
+    const int row = 16 * r + a * C::RPI + lane / C::CH;
+    const int chunk = (lane % C::CH) ^ (row % C::CH);
+    dma16(rs, (uint32_t)row * rowbytes + 16u * chunk,
+          lds_tile + (uint32_t)((16 * r + a * C::RPI) * C::ROWB));
+  }
+}
 
-  // fp32 state rows owned by this wave, as MFMA accumulators:
-  // kv[rt][ct][i] = KV[DK0 + 16 rt + 4 g + i][c0 + 16 ct + l16].
-  f32x4 kv[RT > 0 ? RT : 1][2];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
-        kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
-      }
-  char *const kvx0 = smem + C::KVX_OFF;
-  auto write_kvx = [&](char *dst) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        *(bf16x4 *)(dst + swz<D>(16 * ct + l16, DK0 + 16 * rt + 4 * g)) = to_bf16x4(kv[rt][ct]);
-  };
-  write_kvx(kvx0);
+// DMA rows 16r..16r+15 of the V slice (32 columns, 64 bytes per row, unswizzled).
+template <int D>
+__device__ __forceinline__ void dma_vrows(const Chain &c, int blk, int r, uint32_t lds_tile,
+                                          int lane) {
+  using C = Cfg<D>;
+  int64_t row0;
+  const int b = block_rows(c, blk, row0);
+  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
+  const auto rs = rsrc(c.v + row0 * D + c.c0, (uint32_t)b * rowbytes);
+  const int row = 16 * r + lane / 4;
+  dma16(rs, (uint32_t)row * rowbytes + 16u * (lane % 4), lds_tile + 16 * r * C::VROWB);
+}
 
-  // Per-lane constants (the same for every full block).
-  float maskw[NT][4];  // lambda^(jrow - j'), j' = 16 t + 4 g + i, for j' <= jrow
-  bool keep[NT][4];
+// ------------------------------------------------------------------------------------------
+// Output wave r: rows 16r..16r+15 of every block.  Issues the DMA of its own Q rows and V rows,
+// and once its V rows of the next block have landed writes them decayed, lambda^(b-1-j) V[j],
+// to the double-buffered copy the state waves consume (so no state wave scales operands).
+// ------------------------------------------------------------------------------------------
+template <int D, int R>
+__device__ __forceinline__ void output_wave(const Chain &c, char *smem, const float *pw,
+                                            int lane) {
+  using C = Cfg<D>;
+  constexpr int NT = R + 1;         // causal score tiles
+  constexpr int NS = (NT + 1) / 2;  // 32-token k-steps of the intra product
+  constexpr int DMA = C::QK_DMA + 1;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int jrow = 16 * R + l16;  // this lane's output row inside a block
+  const uint32_t smem_lds = lds_addr(smem);
+
+  // Decay weights lambda^(jrow - j'), j' = 16 t + 4 g + i; only the diagonal tile t = R has
+  // entries above the diagonal (j' > jrow), which are selected away.
+  float maskw[NT][4];
+  bool keep[4];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int jp = 16 * t + 4 * g + i;
-      keep[t][i] = jp <= jrow;
-      maskw[t][i] = keep[t][i] ? pw[jrow - jp] : 0.f;
+      maskw[t][i] = jp <= jrow ? pw[jrow - jp] : 0.f;
+      if (t == R) keep[i] = jp <= jrow;
     }
   const float inter_scale = pw[jrow + 1];
-  // Token of element e of this lane's 32-token k-step s: 32 s + 4 g + e (e < 4) and
-  // 32 s + 16 + 4 g + (e - 4) (e >= 4); lambda^(BLK-1-tok) for a full block.
-  float ksc_full[2][8];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = 32 * s + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-      ksc_full[s][e] = pw[BLK - 1 - tok];
-    }
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
   const uint32_t rowbytes = (uint32_t)c.H * D * 2;
+  // This lane's 16 bytes of the V rows this wave loads: row vrow, bytes 16 (lane % 4) .. +15.
+  const int vrow = 16 * R + lane / 4;
+  const int vbyte = vrow * C::VROWB + 16 * (lane % 4);
+  const int b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
+  const float lv_full = pw[BLK - 1 - vrow];
+  const float lv_last = vrow < b_last ? pw[b_last - 1 - vrow] : 0.f;
 
-  // Prologue: blocks 0 .. NST-2 in flight; wait for block 0.
+  auto issue = [&](int blk) {
+    const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
+    dma_rows<D>(c.q, c, blk, R, st + C::Q_OFF, lane);
+    dma_vrows<D>(c, blk, R, st + C::V_OFF, lane);
+  };
+  // Decayed copy of this wave's V rows of block blk (landed) into buffer blk & 1.
+  auto decay_v = [&](int blk) {
+    const bf16x8 x = *(const bf16x8 *)(smem + (blk % NST) * C::STAGE + C::V_OFF + vbyte);
+    *(bf16x8 *)(smem + C::LV_OFF + (blk & 1) * C::LV + vbyte) =
+        scale8(x, blk == c.nb - 1 ? lv_last : lv_full);
+  };
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) dma_block<D>(c, s, smem + s * C::STAGE, W, lane);
-  wait_vm_barrier<(NST - 2) * (2 * C::QK_DMA + 1)>();
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  wait_vm<(NST - 2) * DMA>();  // own block-0 rows landed
+  decay_v(0);
+  lds_barrier();  // block 0 and its decayed V visible to all waves
 
   for (int i = 0; i < c.nb; ++i) {
-    const int cur = i % NST;
-    const int64_t rem = c.n - (int64_t)i * BLK;
-    const int b = rem < BLK ? (int)rem : BLK;
-    // Refill the stage consumed in step i-1 (every wave has passed the barrier since).
-    dma_block<D>(c, i + NST - 1, smem + ((i + NST - 1) % NST) * C::STAGE, W, lane);
-    const char *Qs = smem + cur * C::STAGE + C::Q_OFF;
-    const char *Ks = smem + cur * C::STAGE + C::K_OFF;
-    const char *Vs = smem + cur * C::STAGE + C::V_OFF;
-    const char *KVs = kvx0 + (i & 1) * C::KVX;
+    issue(i + NST - 1);  // refills the stage read in step i-1
+    const char *stage = smem + (i % NST) * C::STAGE;
+    const char *Qs = stage + C::Q_OFF;
+    const char *Ks = stage + C::K_OFF;
+    const char *Vs = stage + C::V_OFF;
+    const char *KVs = smem + C::KVX_OFF + (i & 1) * C::KVX;
 
     // Q operand (B of S^T and of the inter product): Q[jrow][32 ks + 8 g + 0..7].
     bf16x8 qop[C::KSTEPS];
@@ -270,7 +288,7 @@ __device__ __forceinline__ void wave_loop(const Chain &c, char *smem, const floa
     for (int ks = 0; ks < C::KSTEPS; ++ks)
       qop[ks] = *(const bf16x8 *)(Qs + swz<D>(jrow, 32 * ks + 8 * g));
 
-    // Intra scores, causal tiles only: S^T[16t + 4g + i][jrow] -> P[jrow][16t + 4g + i].
+    // S^T[16t + 4g + i][jrow] = P[jrow][16t + 4g + i] before masking.
     f32x4 sacc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -290,10 +308,10 @@ __device__ __forceinline__ void wave_loop(const Chain &c, char *smem, const floa
         o[ct] = mfma(*(const bf16x8 *)(KVs + swz<D>(16 * ct + l16, 32 * ks + 8 * g)), qop[ks],
                      o[ct]);
 
-    // V operands, token-major: vop[s][ct] lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
-    bf16x8 vop[2][2];
+    // V operands of the causal k-steps: lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
+    bf16x8 vop[NS][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROWB + 2 * (16 * ct + tcol));
@@ -301,22 +319,24 @@ __device__ __forceinline__ void wave_loop(const Chain &c, char *smem, const floa
         vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 
-    // Decay/causal mask in registers (select), then P in bf16.
-    bf16x4 p[2 * ((NT + 1) / 2)];
+    // Decay/causal mask in registers, then P in bf16 (tiles past the diagonal are zero).
+    bf16x4 p[2 * NS];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      f32x4 m;
+      f32x4 m = sacc[t] * f32x4{maskw[t][0], maskw[t][1], maskw[t][2], maskw[t][3]};
+      if (t == R) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m[e] = keep[t][e] ? sacc[t][e] * maskw[t][e] : 0.f;
+        for (int e = 0; e < 4; ++e) m[e] = keep[e] ? m[e] : 0.f;
+      }
       p[t] = to_bf16x4(m);
     }
     if constexpr (NT % 2) p[NT] = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 
-    // O^T = lambda^(j+1) * inter + V^T P^T over the causal k-steps.
+    // O^T = lambda^(j+1) * inter + V^T P^T.
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) o[ct] *= inter_scale;
 #pragma unroll
-    for (int s = 0; s < (NT + 1) / 2; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const bf16x8 pop = __builtin_shufflevector(p[2 * s], p[2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) o[ct] = mfma(vop[s][ct], pop, o[ct]);
@@ -324,6 +344,8 @@ __device__ __forceinline__ void wave_loop(const Chain &c, char *smem, const floa
 
     // Store: lane holds O[jrow][c0 + 16ct + 4g + 0..3]; rows past the end are dropped.
     {
+      const int64_t rem = c.n - (int64_t)i * BLK;
+      const int b = rem < BLK ? (int)rem : BLK;
       const int64_t row0 = (c.tok0 + (int64_t)i * BLK) * c.H + c.h;
       const auto ro = rsrc(c.out + row0 * D + c.c0, (uint32_t)b * rowbytes);
       const uint32_t off = (uint32_t)jrow * rowbytes + 8u * g;
@@ -333,61 +355,98 @@ __device__ __forceinline__ void wave_loop(const Chain &c, char *smem, const floa
                                               off + 32u * ct, 0, 0);
     }
 
-    // State update: KV = lambda^b KV + K^T diag(lambda^(b-1-tok)) V.
-    if (RT > 0) {
-      float ksc[2][8];
-      if (b == BLK) {
+    // Own rows of block i+1 landed: its DMA was issued in step i-1 (or the prologue); since
+    // then this wave issued that step's 2 stores, this step's DMA and 2 stores.
+    static_assert(NST == 3, "wait counts are written for three stages");
+    if (i == 0) wait_vm<DMA + 2>();
+    else wait_vm<DMA + 4>();
+    decay_v(i + 1);
+    lds_barrier();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // DMAs in flight target this LDS
+}
+
+// ------------------------------------------------------------------------------------------
+// State wave r: its band of the fp32 state.  Issues the DMA of K rows 16r..16r+15.
+// ------------------------------------------------------------------------------------------
+template <int D, int R>
+__device__ __forceinline__ void state_wave(const Chain &c, char *smem, const float *pw,
+                                           const float *s0, float *fs, size_t sbase, int lane) {
+  using C = Cfg<D>;
+  using Bd = Band<D, R>;
+  constexpr int RT = Bd::RT;
+  constexpr int DK0 = Bd::DK0;
+  constexpr int DMA = C::QK_DMA;
+  const int l16 = lane & 15, g = lane >> 4;
+  const uint32_t smem_lds = lds_addr(smem);
+
+  // kv[rt][ct][i] = KV[DK0 + 16 rt + 4 g + i][c0 + 16 ct + l16].
+  f32x4 kv[RT > 0 ? RT : 1][2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ksc[s][e] = ksc_full[s][e];
-      } else {
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int tok = 32 * s + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-            ksc[s][e] = tok < b ? pw[b - 1 - tok] : 0.f;
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
+        kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
       }
-      const float lb = pw[b];
+  auto write_kvx = [&](char *dst) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        *(bf16x4 *)(dst + swz<D>(16 * ct + l16, DK0 + 16 * rt + 4 * g)) = to_bf16x4(kv[rt][ct]);
+  };
+  write_kvx(smem + C::KVX_OFF);
+
+  // lambda^b for full blocks and for the last block, which may be partial (b_last rows).
+  const int b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
+  const float lb_full = pw[BLK], lb_last = pw[b_last];
+  const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
+
+  auto issue = [&](int blk) {
+    const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
+    dma_rows<D>(c.k, c, blk, R, st + C::K_OFF, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  wait_vm_barrier<(NST - 2) * DMA>();
+
+  for (int i = 0; i < c.nb; ++i) {
+    issue(i + NST - 1);
+    const char *Ks = smem + (i % NST) * C::STAGE + C::K_OFF;
+    const char *LVs = smem + C::LV_OFF + (i & 1) * C::LV;  // lambda^(b-1-j) V[j]
+    if constexpr (RT > 0) {
+      const float lb = i == c.nb - 1 ? lb_last : lb_full;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) kv[rt][ct] *= lb;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
+        bf16x8 vop[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const bf16x4 lo = tr_read(LVs + (32 * s + trow) * C::VROWB + 2 * (16 * ct + tcol));
+          const bf16x4 hi = tr_read(LVs + (32 * s + 16 + trow) * C::VROWB + 2 * (16 * ct + tcol));
+          vop[ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int col = DK0 + 16 * rt + tcol;
           const bf16x4 lo = tr_read(Ks + swz<D>(32 * s + trow, col));
           const bf16x4 hi = tr_read(Ks + swz<D>(32 * s + 16 + trow, col));
-          bf16x8 kop;
+          const bf16x8 kop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kop[e] = (__bf16)((float)lo[e] * ksc[s][e]);
-            kop[e + 4] = (__bf16)((float)hi[e] * ksc[s][e + 4]);
-          }
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) kv[rt][ct] = mfma(kop, vop[s][ct], kv[rt][ct]);
+          for (int ct = 0; ct < 2; ++ct) kv[rt][ct] = mfma(kop, vop[ct], kv[rt][ct]);
         }
       }
+      write_kvx(smem + C::KVX_OFF + ((i + 1) & 1) * C::KVX);
     }
-
-    // Publish the new state (bf16) for the next block's inter product; wait until block i+1
-    // has landed in LDS (its DMA was issued NST-2 steps ago, or in the prologue).
-    write_kvx(kvx0 + ((i + 1) & 1) * C::KVX);
-    constexpr int DMA = 2 * C::QK_DMA + 1;
-    constexpr int PER = C::VMEM_PER_STEP;
-    if (NST == 3) {
-      if (i == 0) wait_vm_barrier<PER>();
-      else wait_vm_barrier<2 + PER>();
-    } else {
-      static_assert(NST == 3, "wait counts are written for three stages");
-      wait_vm_barrier<DMA>();
-    }
+    // Block i+1's K rows landed: since their DMA this wave issued only this step's DMA.
+    wait_vm_barrier<(NST - 2) * DMA>();
   }
-  // Drain the DMAs still in flight (they target this workgroup's LDS) before leaving.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (fs) {
@@ -412,7 +471,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
-  __shared__ float pw[BLK + 1];  // lambda^m, m = 0..BLK
+  // lambda^m, m = 0..BLK: lives in the last stage until that stage's first DMA, which every
+  // wave issues only after it has copied the powers it needs into registers.
+  float *const pw = (float *)(smem + (NST - 1) * C::STAGE);
 
   // Workgroup -> (chain = sequence*H + head, value slice); slices of a chain share an XCD.
   const int total = S * H * NS;
@@ -441,23 +502,29 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   c.c0 = slice * CV;
 
   const int tid = threadIdx.x;
+  // Zero the stages once: rows a partial block does not load then hold zeros or finite values
+  // of earlier blocks, never stale bits from another kernel.
+  for (int off = 16 * tid; off < NST * C::STAGE; off += 16 * NTHR)
+    *(u32x4 *)(smem + off) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
   if (tid <= BLK) {
     const float lam = decay[h];
     double p = 1.0;  // lambda^tid by repeated multiplication (0^0 = 1)
     for (int i = 0; i < tid; ++i) p *= (double)lam;
     pw[tid] = (float)p;
   }
-  // Zero the stages once: rows a partial block does not load then hold zeros or finite values
-  // of earlier blocks, never stale bits from another kernel.
-  for (int off = 16 * tid; off < C::NST * C::STAGE; off += 16 * NTHR)
-    *(u32x4 *)(smem + off) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();  // pw and zeroed stages visible before any DMA or read
   const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
+  const int lane = tid & 63;
   switch (tid >> 6) {
-    case 0: wave_loop<D, 0>(c, smem, pw, s0, fs, sbase, tid); break;
-    case 1: wave_loop<D, 1>(c, smem, pw, s0, fs, sbase, tid); break;
-    case 2: wave_loop<D, 2>(c, smem, pw, s0, fs, sbase, tid); break;
-    default: wave_loop<D, 3>(c, smem, pw, s0, fs, sbase, tid); break;
+    case 0: output_wave<D, 0>(c, smem, pw, lane); break;
+    case 1: output_wave<D, 1>(c, smem, pw, lane); break;
+    case 2: output_wave<D, 2>(c, smem, pw, lane); break;
+    case 3: output_wave<D, 3>(c, smem, pw, lane); break;
+    case 4: state_wave<D, 0>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 5: state_wave<D, 1>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 6: state_wave<D, 2>(c, smem, pw, s0, fs, sbase, lane); break;
+    default: state_wave<D, 3>(c, smem, pw, s0, fs, sbase, lane); break;
   }
 }
 
