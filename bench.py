@@ -157,13 +157,29 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "prefill_bf16_kernel<128>",
             "achieved": pre_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": pre_gbps / HBM_PEAK_GBPS, "traffic": None,
+            "frac": pre_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
         },
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter runs (profiles/traffic.json),
+    or None when the kernel source has changed since those counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        doc = json.load(open(path))
+        src = open(os.path.join(ROOT, doc["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != doc.get("kernel_source_sha256"):
+        return None
+    return doc.get("traffic_bytes_per_launch")
 
 
 def copy_probe(mib, steps, warmup):

@@ -83,8 +83,8 @@ def test_prefill_8k_full_quadratic():
     ref_s = oracle.final_state(k, v, decay)
     e = slice_errors(to_np(out), ref, [0, wl.T])
     es = state_errors(to_np(fs), ref_s)
-    print("prefill_8k per-head out errors:", np.array2string(e[0], precision=2))
-    print("prefill_8k per-head state errors:", np.array2string(es[0], precision=2))
+    print("prefill_8k per-head out errors:", np.array2string(e[0], formatter={"float_kind": lambda x: "%.2e" % x}))
+    print("prefill_8k per-head state errors:", np.array2string(es[0], formatter={"float_kind": lambda x: "%.2e" % x}))
     assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
 
 

@@ -84,8 +84,8 @@ def test_prefill_1m_sampled_heads():
     ref, ref_s = oracle.recurrent(qh, kh, vh, decay[hs])
     e = slice_errors(to_np(oh), ref, [0, wl.T])
     es = state_errors(to_np(fs[:, hs]), ref_s)
-    print("prefill_1m: out", np.array2string(e[0], precision=2), "state",
-          np.array2string(es[0], precision=2))
+    print("prefill_1m: out", np.array2string(e[0], formatter={"float_kind": lambda x: "%.2e" % x}), "state",
+          np.array2string(es[0], formatter={"float_kind": lambda x: "%.2e" % x}))
     assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
 
 
