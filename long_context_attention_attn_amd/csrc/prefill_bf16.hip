@@ -74,7 +74,8 @@ struct Cfg {
   static constexpr int KVX_OFF = NST * STAGE;
   static constexpr int LV = BLK * VROWB;                   // decayed V copy, [BLK][CV]
   static constexpr int LV_OFF = NST * STAGE + 2 * KVX;
-  static constexpr int SMEM = NST * STAGE + 2 * KVX + 2 * LV;
+  static constexpr int PF_OFF = LV_OFF + 2 * LV;           // 1 KiB sink of the L2 prefetches
+  static constexpr int SMEM = PF_OFF + 1024;
 };
 
 // State rows owned by state wave R (in 16-row tiles) and its first row.  Output wave r does
@@ -178,6 +179,7 @@ struct Chain {
   int64_t n;     // its length
   int nb;        // number of blocks
   int H, h, c0;  // heads, this head, first value column of the slice
+  int slice;     // c0 / CV
 };
 
 // Rows of block `blk` that exist (0 past the end) and the element offset of its first row.
@@ -219,10 +221,32 @@ __device__ __forceinline__ void dma_vrows(const Chain &c, int blk, int r, uint32
   dma16(rs, (uint32_t)row * rowbytes + 16u * (lane % 4), lds_tile + 16 * r * C::VROWB);
 }
 
+// Pull block `blk`'s rows 16s..16s+15 (s = this workgroup's value slice) of q, k and of the full
+// v rows into L2, several blocks before their DMA: one 16-byte read per 128-byte line, written to
+// a scratch area of LDS that nothing reads.  The D/32 slices of a head together cover all 64 rows
+// once, and the later DMAs of all four slices then hit L2 instead of waiting on HBM.
+template <int D>
+__device__ __forceinline__ void prefetch_l2(const Chain &c, int blk, uint32_t sink, int lane) {
+  int64_t row0;
+  const int b = block_rows(c, blk, row0);
+  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
+  const uint32_t bytes = (uint32_t)b * rowbytes;
+  const int row = 16 * c.slice + ((lane >> 1) & 15);
+  const uint32_t off = (uint32_t)row * rowbytes + (uint32_t)(lane & 1) * (D == 128 ? 128u : 64u);
+  dma16(rsrc(c.q + row0 * D, bytes), off, sink);
+  dma16(rsrc(c.k + row0 * D, bytes), off, sink);
+  dma16(rsrc(c.v + row0 * D, bytes), off, sink);
+}
+constexpr int PF_DMA = 3;   // prefetch instructions per block
+constexpr int PF_AHEAD = 4; // blocks between a block's prefetch and its DMA
+
 // ------------------------------------------------------------------------------------------
-// Output wave r: rows 16r..16r+15 of every block.  Issues the DMA of its own Q rows and V rows,
-// and once its V rows of the next block have landed writes them decayed, lambda^(b-1-j) V[j],
-// to the double-buffered copy the state waves consume (so no state wave scales operands).
+// Output wave r: rows 16r..16r+15 of every block.  The loading duties are dealt against the
+// score work (wave r does r+1 score tiles): wave 0 loads Q rows 0..15 and V rows 0..31, wave 1
+// Q rows 16..31 and 48..63 and V rows 32..47, wave 2 Q rows 32..47 and V rows 48..63, wave 3
+// (four score tiles) nothing.  Once its V rows of the next block have landed, a wave writes them
+// decayed, lambda^(b-1-j) V[j], to the double-buffered copy the state waves consume (so no state
+// wave scales operands).
 // ------------------------------------------------------------------------------------------
 template <int D, int R>
 __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const float *pw,
@@ -230,7 +254,11 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
   using C = Cfg<D>;
   constexpr int NT = R + 1;         // causal score tiles
   constexpr int NS = (NT + 1) / 2;  // 32-token k-steps of the intra product
-  constexpr int DMA = C::QK_DMA + 1;
+  // DMA instructions this wave issues per block.
+  constexpr int DMA = R == 0 ? C::QK_DMA + 2 : R == 1 ? 2 * C::QK_DMA + 1 : R == 2 ? C::QK_DMA + 1 : 0;
+  // 16-row groups of V this wave loads and decays: [VG0, VG0 + NVG).
+  constexpr int VG0 = R == 0 ? 0 : R == 1 ? 2 : 3;
+  constexpr int NVG = R == 0 ? 2 : R == 3 ? 0 : 1;
   const int l16 = lane & 15, g = lane >> 4;
   const int jrow = 16 * R + l16;  // this lane's output row inside a block
   const uint32_t smem_lds = lds_addr(smem);
@@ -250,27 +278,43 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
   const float inter_scale = pw[jrow + 1];
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
   const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  // This lane's 16 bytes of the V rows this wave loads: row vrow, bytes 16 (lane % 4) .. +15.
-  const int vrow = 16 * R + lane / 4;
-  const int vbyte = vrow * C::VROWB + 16 * (lane % 4);
+  // This wave's share of the decayed V copy: lane bytes 16 (lane % 4) .. +15 of V rows
+  // 16 m + lane / 4, m in its groups, with their decay lambda^(b-1-row) (full and last block).
   const int b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
-  const float lv_full = pw[BLK - 1 - vrow];
-  const float lv_last = vrow < b_last ? pw[b_last - 1 - vrow] : 0.f;
+  float lv_full[NVG > 0 ? NVG : 1], lv_last[NVG > 0 ? NVG : 1];
+#pragma unroll
+  for (int m = 0; m < NVG; ++m) {
+    const int vrow = 16 * (VG0 + m) + lane / 4;
+    lv_full[m] = pw[BLK - 1 - vrow];
+    lv_last[m] = vrow < b_last ? pw[b_last - 1 - vrow] : 0.f;
+  }
 
   auto issue = [&](int blk) {
     const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
-    dma_rows<D>(c.q, c, blk, R, st + C::Q_OFF, lane);
-    dma_vrows<D>(c, blk, R, st + C::V_OFF, lane);
+    if constexpr (R < 3) dma_rows<D>(c.q, c, blk, R, st + C::Q_OFF, lane);
+    if constexpr (R == 1) dma_rows<D>(c.q, c, blk, 3, st + C::Q_OFF, lane);
+#pragma unroll
+    for (int m = 0; m < NVG; ++m) dma_vrows<D>(c, blk, VG0 + m, st + C::V_OFF, lane);
   };
-  // Decayed copy of this wave's V rows of block blk (landed) into buffer blk & 1.
+  // Decayed copy of this wave's V rows of block blk (landed) into buffer blk & 1.  All reads
+  // are issued before any write, so the LDS round trips overlap.
   auto decay_v = [&](int blk) {
-    const bf16x8 x = *(const bf16x8 *)(smem + (blk % NST) * C::STAGE + C::V_OFF + vbyte);
-    *(bf16x8 *)(smem + C::LV_OFF + (blk & 1) * C::LV + vbyte) =
-        scale8(x, blk == c.nb - 1 ? lv_last : lv_full);
+    if constexpr (NVG > 0) {
+      const bool last = blk == c.nb - 1;
+      bf16x8 x[NVG];
+#pragma unroll
+      for (int m = 0; m < NVG; ++m)
+        x[m] = *(const bf16x8 *)(smem + (blk % NST) * C::STAGE + C::V_OFF +
+                                 (16 * (VG0 + m) + lane / 4) * C::VROWB + 16 * (lane % 4));
+#pragma unroll
+      for (int m = 0; m < NVG; ++m)
+        *(bf16x8 *)(smem + C::LV_OFF + (blk & 1) * C::LV + (16 * (VG0 + m) + lane / 4) * C::VROWB +
+                    16 * (lane % 4)) = scale8(x[m], last ? lv_last[m] : lv_full[m]);
+    }
   };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s);
-  wait_vm<(NST - 2) * DMA>();  // own block-0 rows landed
+  if constexpr (DMA > 0) wait_vm<(NST - 2) * DMA>();  // own block-0 rows landed
   decay_v(0);
   lds_barrier();  // block 0 and its decayed V visible to all waves
 
@@ -358,8 +402,10 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
     // Own rows of block i+1 landed: its DMA was issued in step i-1 (or the prologue); since
     // then this wave issued that step's 2 stores, this step's DMA and 2 stores.
     static_assert(NST == 3, "wait counts are written for three stages");
-    if (i == 0) wait_vm<DMA + 2>();
-    else wait_vm<DMA + 4>();
+    if constexpr (DMA > 0) {
+      if (i == 0) wait_vm<DMA + 2>();
+      else wait_vm<DMA + 4>();
+    }
     decay_v(i + 1);
     lds_barrier();
   }
@@ -367,7 +413,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 }
 
 // ------------------------------------------------------------------------------------------
-// State wave r: its band of the fp32 state.  Issues the DMA of K rows 16r..16r+15.
+// State wave r: its band of the fp32 state.  Issues the DMA of K rows 16r..16r+15; the lightest
+// state wave (r = 3) also issues the L2 prefetches.
 // ------------------------------------------------------------------------------------------
 template <int D, int R>
 __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const float *pw,
@@ -376,7 +423,11 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   using Bd = Band<D, R>;
   constexpr int RT = Bd::RT;
   constexpr int DK0 = Bd::DK0;
-  constexpr int DMA = C::QK_DMA;
+  constexpr bool PF = R == 3;
+  constexpr int DMA = C::QK_DMA + (PF ? PF_DMA : 0);
+  // Operations issued after a block's K DMA until the wait for it: the NST-2 later issues, plus,
+  // with prefetches (issued after the K DMA of the same block), that block's own prefetches.
+  constexpr int WAIT = (NST - 2) * DMA + (PF ? PF_DMA : 0);
   const int l16 = lane & 15, g = lane >> 4;
   const uint32_t smem_lds = lds_addr(smem);
 
@@ -408,10 +459,18 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   auto issue = [&](int blk) {
     const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
     dma_rows<D>(c.k, c, blk, R, st + C::K_OFF, lane);
+    // after the DMA, so that waiting for this DMA never waits for a prefetch (counters are
+    // in order)
+    if constexpr (PF) prefetch_l2<D>(c, blk + PF_AHEAD, smem_lds + C::PF_OFF, lane);
   };
+  if constexpr (PF) {
+    // Blocks NST-1 .. PF_AHEAD-1 are not covered by the prefetches of the first issues.
+    for (int blk = NST - 1; blk < PF_AHEAD; ++blk)
+      prefetch_l2<D>(c, blk, smem_lds + C::PF_OFF, lane);
+  }
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s);
-  wait_vm_barrier<(NST - 2) * DMA>();
+  wait_vm_barrier<WAIT>();
 
   for (int i = 0; i < c.nb; ++i) {
     issue(i + NST - 1);
@@ -444,8 +503,8 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
       }
       write_kvx(smem + C::KVX_OFF + ((i + 1) & 1) * C::KVX);
     }
-    // Block i+1's K rows landed: since their DMA this wave issued only this step's DMA.
-    wait_vm_barrier<(NST - 2) * DMA>();
+    // Block i+1's K rows landed: since their DMA this wave issued only the later issues.
+    wait_vm_barrier<WAIT>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -500,6 +559,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   c.H = H;
   c.h = h;
   c.c0 = slice * CV;
+  c.slice = slice;
 
   const int tid = threadIdx.x;
   // Zero the stages once: rows a partial block does not load then hold zeros or finite values
