@@ -54,6 +54,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the few-chain sequence-split timings (outside the timed steps)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, time a plain device-to-device copy of this "
@@ -161,9 +163,58 @@ def main():
         },
     }
 
+    if not args.no_extras:
+        del q, k, v, out
+        result["few_chain_prefill"] = few_chain_prefill(dev)
     if not args.no_cpu_baseline:
+        q, k, v = wl.inputs(device=dev)
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)
     print(json.dumps(result), flush=True)
+
+
+def time_ms(fn, iters, warmup):
+    """Average milliseconds per call from HIP events on the current stream (the library's
+    kernels run on it)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def few_chain_prefill(dev, iters=20, warmup=3):
+    """Prefill shapes with few (sequence, head) chains -- 8,192 x 8 heads and 65,536 x 8 heads
+    (one device's share of the 64-head layer under 8-way head sharding) -- timed with the plain
+    scan and with the sequence split the library suggests."""
+    import torch
+
+    import long_context_attention_attn_amd as la
+    from long_context_attention_attn_amd import _lib, synth
+
+    res = []
+    for T, Hc in ((8192, 8), (65536, 8)):
+        q, k, v = synth.qkv(T, Hc, D, torch.bfloat16, seed=0, device=dev)
+        dec = synth.decay_geometric(Hc, 0.9, 0.9999).to(dev)
+        o = torch.empty_like(q)
+        f = torch.empty((1, Hc, D, D), dtype=torch.float32, device=dev)
+        seg = _lib.prefill_split_blocks(T, 1, Hc, D)
+        plain = time_ms(lambda: la.prefill(q, k, v, dec, out=o, final_state=f), iters, warmup)
+        split = time_ms(lambda: la.prefill(q, k, v, dec, out=o, final_state=f, split=seg or None),
+                        iters, warmup)
+        nbytes = prefill_bytes(T, Hc, D)
+        res.append({"tokens": T, "heads": Hc, "seg_blocks": seg, "plain_ms": plain,
+                    "split_ms": split, "speedup": plain / split,
+                    "split_algorithmic_GBps": nbytes / (split / 1e3) / 1e9,
+                    "split_tokens_per_s": T / (split / 1e3)})
+        del q, k, v, o
+    return res
 
 
 def measured_traffic():

@@ -43,6 +43,7 @@
 #ifndef LIGHTNING_ATTN_H
 #define LIGHTNING_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -85,6 +86,49 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
                         const int32_t *cu_seqlens, const float *initial_state, void *out,
                         float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
                         la_dtype dtype, void *stream);
+
+/*
+ * Sequence-split prefill: the same result as la_prefill_ex, computed with every sequence cut
+ * into segments of seg_blocks * 64 tokens that are scanned in parallel.  Meant for batches with
+ * few (sequence, head) pairs, where the plain prefill runs one workgroup per (sequence, head,
+ * 32 value columns) and leaves most of the device idle.
+ *
+ * The block recurrence (digest, section 1: the running state of the right product) is linear
+ * in the state, so a segment of m tokens maps its incoming state S_in to lambda^m S_in + L with
+ * L independent of S_in.  Four launches on `stream`: a segment table built from cu_seqlens on
+ * the device; L of every segment (k and v read once); a combine that walks each sequence's
+ * segments in order (incoming state of the first = initial_state or 0, final state = what
+ * follows the last); the prefill of every segment from its incoming state.  q, k and v are read
+ * twice in total (k and v in both scans), out is written once.  The result differs from
+ * la_prefill_ex only in rounding order.
+ *
+ *   seg_blocks       >= 1: segment length in 64-token blocks (la_prefill_split_blocks suggests
+ *                    one for the current device)
+ *   workspace        device memory of at least la_prefill_split_workspace_size(...) bytes,
+ *                    256-byte aligned, owned by the caller; holds the segment states and the
+ *                    segment table between the launches (no initial contents needed; not
+ *                    read after the call's work on `stream` completes).  Calls that share a
+ *                    workspace must be ordered (same stream).
+ *   T < 2^31 (segment starts are int32); all other arguments as la_prefill_ex.
+ * Errors: as la_prefill_ex, plus LA_ERR_INVALID_ARG for seg_blocks < 1, a NULL, misaligned or
+ * too small workspace, T >= 2^31 or more than 2^31 segment workgroups.
+ */
+la_status la_prefill_split(const void *q, const void *k, const void *v, const float *decay,
+                           const int32_t *cu_seqlens, const float *initial_state, void *out,
+                           float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                           la_dtype dtype, int32_t seg_blocks, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Workspace bytes la_prefill_split needs for these sizes (0 for invalid sizes).  The bound
+ * holds for any valid cu_seqlens: (ceil(T / (64 seg_blocks)) + S - 1) states of H*D*D floats
+ * plus the segment table. */
+size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t D,
+                                       int32_t seg_blocks);
+
+/* Suggested seg_blocks for the current device: about one segment workgroup per compute unit,
+ * at least 4 blocks per segment; 0 when splitting would not add parallelism (the plain launch
+ * already has a workgroup per compute unit, or no sequence would be cut) or on any error. */
+int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D);
 
 /*
  * One recurrent decode step for Bt independent sequences (one new token each):

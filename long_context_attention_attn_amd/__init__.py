@@ -15,7 +15,7 @@ Decode updates the fixed-size state once per token: S' = lambda S + k^T v, o = q
 """
 from __future__ import annotations
 
-from typing import Optional, Tuple
+from typing import Optional, Tuple, Union
 
 import torch
 
@@ -49,13 +49,19 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
             initial_state: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None,
-            return_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            return_final_state: bool = True,
+            split: Union[None, str, int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Lightning-attention prefill over packed sequences.
 
     q, k, v: [T, H, D] bf16 or fp32 (same dtype), contiguous, on a gfx950 device.
     decay: [H] fp32 on the same device.  cu_seqlens: [S+1] int32 on the device, or None for
     one sequence.  initial_state: optional [S, H, D, D] fp32.  Returns (out [T, H, D],
     final_state [S, H, D, D] fp32 or None).  Runs asynchronously on the current stream.
+
+    split: None = one scan per (sequence, head); an int n >= 1 = the sequence-split prefill
+    with segments of n 64-token blocks (a workspace is allocated with torch); "auto" = the
+    sequence split with the segment length the library suggests for this device, or the plain
+    scan when it suggests none.  All give the same result up to rounding order.
     """
     device = q.device
     if q.dim() != 3:
@@ -95,11 +101,26 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
         _check_act("final_state", final_state, torch.float32, device)
         if final_state.shape != (S, H, D, D):
             raise ValueError("final_state must be [S, H, D, D]")
-    _lib.prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
-                    0 if cu_seqlens is None else cu_seqlens.data_ptr(),
-                    0 if initial_state is None else initial_state.data_ptr(),
-                    out.data_ptr(), 0 if final_state is None else final_state.data_ptr(),
-                    T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
+    seg_blocks = 0
+    if split == "auto":
+        seg_blocks = _lib.prefill_split_blocks(T, S, H, D)
+    elif split is not None:
+        if isinstance(split, bool) or not isinstance(split, int) or split < 1:
+            raise ValueError("split must be None, 'auto' or an int >= 1")
+        seg_blocks = split
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
+            0 if cu_seqlens is None else cu_seqlens.data_ptr(),
+            0 if initial_state is None else initial_state.data_ptr(),
+            out.data_ptr(), 0 if final_state is None else final_state.data_ptr())
+    if seg_blocks > 0:
+        nbytes = _lib.prefill_split_workspace_size(T, S, H, D, seg_blocks)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        # ws is allocated on the current stream, so torch's caching allocator reuses its memory
+        # only for work queued after these kernels on that stream
+        _lib.prefill_split(*ptrs, T, S, H, D, _DTYPES[dtype], seg_blocks, ws.data_ptr(), nbytes,
+                           _stream_ptr(device))
+    else:
+        _lib.prefill_ex(*ptrs, T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
     return out, final_state
 
 

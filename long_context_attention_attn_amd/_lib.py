@@ -20,8 +20,9 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
 
 # Every symbol declared in include/lightning_attn.h.
-EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_decode_step", "la_status_str",
-           "la_last_error")
+EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_split",
+           "la_prefill_split_workspace_size", "la_prefill_split_blocks", "la_decode_step",
+           "la_status_str", "la_last_error")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +64,13 @@ def load():
         lib.la_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
                                       ctypes.c_int, vp]
         lib.la_prefill_ex.restype = ctypes.c_int
+        lib.la_prefill_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
+                                         ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
+        lib.la_prefill_split.restype = ctypes.c_int
+        lib.la_prefill_split_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+        lib.la_prefill_split_workspace_size.restype = ctypes.c_size_t
+        lib.la_prefill_split_blocks.argtypes = [i64, i32, i32, i32]
+        lib.la_prefill_split_blocks.restype = i32
         lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_status_str.argtypes = [ctypes.c_int]
@@ -92,6 +100,21 @@ def prefill_ex(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S
                stream):
     _raise(load().la_prefill_ex(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens), _p(initial_state),
                                 _p(out), _p(final_state), T, S, H, D, dtype, _p(stream)))
+
+
+def prefill_split(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H, D, dtype,
+                  seg_blocks, workspace, workspace_bytes, stream):
+    _raise(load().la_prefill_split(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens),
+                                   _p(initial_state), _p(out), _p(final_state), T, S, H, D, dtype,
+                                   seg_blocks, _p(workspace), workspace_bytes, _p(stream)))
+
+
+def prefill_split_workspace_size(T, S, H, D, seg_blocks) -> int:
+    return int(load().la_prefill_split_workspace_size(T, S, H, D, seg_blocks))
+
+
+def prefill_split_blocks(T, S, H, D) -> int:
+    return int(load().la_prefill_split_blocks(T, S, H, D))
 
 
 def decode_step(q, k, v, decay, state, out, Bt, H, D, dtype, stream):

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning_attn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["la_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["la_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "split.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

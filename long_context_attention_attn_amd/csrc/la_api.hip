@@ -28,10 +28,12 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
-int g_dev_ok[kMaxDevices];  // 1 = gfx950, 0 = other arch
+int g_dev_ok[kMaxDevices];   // 1 = gfx950, 0 = other arch
+int g_dev_cus[kMaxDevices];  // compute units
 
-// Checks that the current device exists and is a gfx950; cached per device.
-la_status check_device() {
+// Checks that the current device exists and is a gfx950; cached per device.  *cus (optional)
+// receives its number of compute units.
+la_status check_device(int *cus = nullptr) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -41,10 +43,12 @@ la_status check_device() {
     hipDeviceProp_t prop;
     perr = hipGetDeviceProperties(&prop, dev);
     g_dev_ok[dev] = (perr == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0);
+    g_dev_cus[dev] = perr == hipSuccess ? prop.multiProcessorCount : 0;
   });
   if (perr != hipSuccess)
     return fail(LA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(perr));
   if (!g_dev_ok[dev]) return fail(LA_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+  if (cus) *cus = g_dev_cus[dev];
   return LA_OK;
 }
 
@@ -64,6 +68,29 @@ la_status check_common(const void *q, const void *k, const void *v, const float 
       return fail(LA_ERR_INVALID_ARG, "tensor too large");
   }
   return LA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Largest number of segments valid cu_seqlens can produce: sum over sequences of
+// ceil(n_s / L) <= ceil(T / L) + S - 1.
+int64_t split_capacity(int64_t T, int32_t S, int64_t seg_len) {
+  return T <= 0 ? 0 : (T + seg_len - 1) / seg_len + S - 1;
+}
+
+struct SplitLayout {
+  int64_t cap;
+  size_t states, seg_cu, seq_seg0, bytes;  // byte offsets and total size
+};
+
+SplitLayout split_layout(int64_t T, int32_t S, int32_t H, int32_t D, int32_t seg_blocks) {
+  SplitLayout l;
+  l.cap = split_capacity(T, S, (int64_t)seg_blocks * 64);
+  l.states = 0;
+  l.seg_cu = align256((size_t)l.cap * H * D * D * sizeof(float));
+  l.seq_seg0 = l.seg_cu + align256((size_t)(l.cap + 1) * sizeof(int32_t));
+  l.bytes = l.seq_seg0 + align256((size_t)(S + 1) * sizeof(int32_t));
+  return l;
 }
 
 }  // namespace
@@ -101,7 +128,7 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
   st = check_device();
   if (st != LA_OK) return st;
 
-  LaPrefillArgs a;
+  LaPrefillArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -125,6 +152,93 @@ la_status la_prefill(const void *q, const void *k, const void *v, const float *d
                      int32_t S, int32_t H, int32_t D, la_dtype dtype, void *stream) {
   return la_prefill_ex(q, k, v, decay, cu_seqlens, nullptr, out, final_state, T, S, H, D, dtype,
                        stream);
+}
+
+size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t D,
+                                       int32_t seg_blocks) {
+  if (T < 0 || S < 1 || H < 1 || (D != 64 && D != 128) || seg_blocks < 1) return 0;
+  return split_layout(T, S, H, D, seg_blocks).bytes;
+}
+
+int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D) {
+  if (T <= 0 || S < 1 || H < 1 || (D != 64 && D != 128)) return 0;
+  int cus = 0;
+  if (check_device(&cus) != LA_OK || cus <= 0) return 0;
+  const int64_t slices = D / 32;
+  if ((int64_t)S * H * slices >= cus) return 0;  // the plain launch fills the device
+  const int64_t blocks = (T + 63) / 64;
+  int64_t seg = (blocks * H * slices + cus - 1) / cus;  // about one workgroup per CU
+  if (seg < 4) seg = 4;                                  // keep segments a few blocks long
+  if (seg >= blocks || seg > 0x7fffffff) return 0;       // no sequence would be cut
+  return (int32_t)seg;
+}
+
+la_status la_prefill_split(const void *q, const void *k, const void *v, const float *decay,
+                           const int32_t *cu_seqlens, const float *initial_state, void *out,
+                           float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                           la_dtype dtype, int32_t seg_blocks, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  g_err[0] = '\0';
+  la_status st = check_common(q, k, v, decay, out, T, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
+  if (cu_seqlens == nullptr && S != 1)
+    return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
+  if (initial_state != nullptr && initial_state == final_state)
+    return fail(LA_ERR_INVALID_ARG, "initial_state aliases final_state");
+  if (seg_blocks < 1) return fail(LA_ERR_INVALID_ARG, "seg_blocks = %d < 1", seg_blocks);
+  if (T > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "split prefill needs T < 2^31");
+  if (T == 0)  // no segments: final states are the initial states (or zeros)
+    return la_prefill_ex(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H,
+                         D, dtype, stream);
+  const SplitLayout lay = split_layout(T, S, H, D, seg_blocks);
+  if (lay.cap * H * (D / 32) > 0x7fffffffLL || (long long)S * H * (D * D / 256) > 0x7fffffffLL)
+    return fail(LA_ERR_INVALID_ARG, "too many segments");
+  if (workspace == nullptr) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(LA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay.bytes)
+    return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                lay.bytes);
+  st = check_device();
+  if (st != LA_OK) return st;
+
+  char *ws = static_cast<char *>(workspace);
+  float *states = reinterpret_cast<float *>(ws + lay.states);
+  int32_t *seg_cu = reinterpret_cast<int32_t *>(ws + lay.seg_cu);
+  int32_t *seq_seg0 = reinterpret_cast<int32_t *>(ws + lay.seq_seg0);
+  const int32_t cap = (int32_t)lay.cap;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto prefill = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
+
+  hipError_t e = la_launch_seg_table(cu_seqlens, T, S, (int64_t)seg_blocks * 64, cap, seg_cu,
+                                     seq_seg0, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment table launch: %s", hipGetErrorString(e));
+  // Segment states from zero: only k and v are read.
+  LaPrefillArgs a{};
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.cu_seqlens = seg_cu;
+  a.final_state = states;
+  a.T = T;
+  a.S = cap;
+  a.H = H;
+  a.D = D;
+  a.state_only = true;
+  e = prefill(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment state launch: %s", hipGetErrorString(e));
+  e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, final_state, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  // Every segment from its incoming state.
+  a.q = q;
+  a.out = out;
+  a.initial_state = states;
+  a.final_state = nullptr;
+  a.state_only = false;
+  e = prefill(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment prefill launch: %s", hipGetErrorString(e));
+  return LA_OK;
 }
 
 la_status la_decode_step(const void *q, const void *k, const void *v, const float *decay,

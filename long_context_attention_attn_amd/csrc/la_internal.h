@@ -14,6 +14,13 @@ struct LaPrefillArgs {
   float *final_state;         // [S][H][D][D] or nullptr
   int64_t T;
   int32_t S, H, D;
+  // Variants of the same scan (all false = the plain forward prefill):
+  bool reverse;          // scan each sequence from its last token to its first (anti-causal):
+                         // local token t is physical token n-1-t of the sequence
+  bool init_inclusive;   // initial state weighted lambda^t (not lambda^(t+1)) at local token t,
+                         // and the final state multiplied by lambda when the sequence is non-empty
+  bool init_transposed;  // read initial_state[s][h][b][a] as element [a][b]
+  bool state_only;       // compute only final_state (q and out unused, may be NULL)
 };
 
 struct LaDecodeArgs {
@@ -29,3 +36,11 @@ hipError_t la_launch_prefill_bf16(const LaPrefillArgs &a, hipStream_t stream);
 hipError_t la_launch_prefill_f32(const LaPrefillArgs &a, hipStream_t stream);
 hipError_t la_launch_decode_bf16(const LaDecodeArgs &a, hipStream_t stream);
 hipError_t la_launch_decode_f32(const LaDecodeArgs &a, hipStream_t stream);
+
+// Sequence split (split.hip).
+hipError_t la_launch_seg_table(const int32_t *cu, int64_t T, int32_t S, int64_t seg_len,
+                               int32_t cap, int32_t *seg_cu, int32_t *seq_seg0,
+                               hipStream_t stream);
+hipError_t la_launch_combine(const float *decay, const int32_t *seg_cu, const int32_t *seq_seg0,
+                             int32_t S, int32_t H, int32_t D, const float *s0, float *st,
+                             float *fs, hipStream_t stream);

@@ -180,14 +180,31 @@ struct Chain {
   int nb;        // number of blocks
   int H, h, c0;  // heads, this head, first value column of the slice
   int slice;     // c0 / CV
+  bool rev;      // local token t is physical token n-1-t (anti-causal scan)
+  bool incl;     // initial state weighted lambda^t, final state times lambda
+  bool s0t;      // initial state read transposed
 };
 
-// Rows of block `blk` that exist (0 past the end) and the element offset of its first row.
-__device__ __forceinline__ int block_rows(const Chain &c, int blk, int64_t &row0) {
+// Where the rows of block `blk` lie: b rows exist (0 past the end); a buffer descriptor based
+// at element offset row0 and b rows long covers exactly them; local row r of the block is at
+// row first + dir * r of that range.  Forward: first = 0, dir = 1.  Reversed scan: the block's
+// local rows are the sequence's physical rows in descending order, first = b - 1, dir = -1, so
+// a local row past the end gets a negative row index, i.e. a byte offset of at least
+// 2^32 - 63 * rowbytes, which the range check rejects like any row past the end.
+struct BlockRows {
+  int b;
+  int64_t row0;
+  int first, dir;
+};
+__device__ __forceinline__ BlockRows block_rows(const Chain &c, int blk) {
   const int64_t rem = c.n - (int64_t)blk * BLK;
   const int b = rem <= 0 ? 0 : (rem < BLK ? (int)rem : BLK);
-  row0 = (c.tok0 + (int64_t)(b > 0 ? blk : 0) * BLK) * c.H + c.h;
-  return b;
+  int64_t t = c.tok0;  // lowest physical token of the block (the sequence start if b = 0)
+  if (b > 0) t += c.rev ? rem - b : (int64_t)blk * BLK;
+  return BlockRows{b, t * c.H + c.h, c.rev ? b - 1 : 0, c.rev ? -1 : 1};
+}
+__device__ __forceinline__ uint32_t row_off(const BlockRows &br, int row, uint32_t rowbytes) {
+  return (uint32_t)((int64_t)(br.first + br.dir * row) * (int64_t)rowbytes);
 }
 
 // DMA 16 rows (16r..16r+15) of a [64][D] tile of block `blk` into its swizzled LDS image.
@@ -195,15 +212,14 @@ template <int D>
 __device__ __forceinline__ void dma_rows(const __bf16 *base, const Chain &c, int blk, int r,
                                          uint32_t lds_tile, int lane) {
   using C = Cfg<D>;
-  int64_t row0;
-  const int b = block_rows(c, blk, row0);
+  const BlockRows br = block_rows(c, blk);
   const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  const auto rs = rsrc(base + row0 * D, (uint32_t)b * rowbytes);
+  const auto rs = rsrc(base + br.row0 * D, (uint32_t)br.b * rowbytes);
 #pragma unroll
   for (int a = 0; a < C::QK_DMA; ++a) {
     const int row = 16 * r + a * C::RPI + lane / C::CH;
     const int chunk = (lane % C::CH) ^ (row % C::CH);
-    dma16(rs, (uint32_t)row * rowbytes + 16u * chunk,
+    dma16(rs, row_off(br, row, rowbytes) + 16u * chunk,
           lds_tile + (uint32_t)((16 * r + a * C::RPI) * C::ROWB));
   }
 }
@@ -213,31 +229,31 @@ template <int D>
 __device__ __forceinline__ void dma_vrows(const Chain &c, int blk, int r, uint32_t lds_tile,
                                           int lane) {
   using C = Cfg<D>;
-  int64_t row0;
-  const int b = block_rows(c, blk, row0);
+  const BlockRows br = block_rows(c, blk);
   const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  const auto rs = rsrc(c.v + row0 * D + c.c0, (uint32_t)b * rowbytes);
+  const auto rs = rsrc(c.v + br.row0 * D + c.c0, (uint32_t)br.b * rowbytes);
   const int row = 16 * r + lane / 4;
-  dma16(rs, (uint32_t)row * rowbytes + 16u * (lane % 4), lds_tile + 16 * r * C::VROWB);
+  dma16(rs, row_off(br, row, rowbytes) + 16u * (lane % 4), lds_tile + 16 * r * C::VROWB);
 }
 
 // Pull block `blk`'s rows 16s..16s+15 (s = this workgroup's value slice) of q, k and of the full
 // v rows into L2, several blocks before their DMA: one 16-byte read per 128-byte line, written to
 // a scratch area of LDS that nothing reads.  The D/32 slices of a head together cover all 64 rows
 // once, and the later DMAs of all four slices then hit L2 instead of waiting on HBM.
-template <int D>
+template <int D, bool SO>
 __device__ __forceinline__ void prefetch_l2(const Chain &c, int blk, uint32_t sink, int lane) {
-  int64_t row0;
-  const int b = block_rows(c, blk, row0);
+  const BlockRows br = block_rows(c, blk);
   const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  const uint32_t bytes = (uint32_t)b * rowbytes;
+  const uint32_t bytes = (uint32_t)br.b * rowbytes;
   const int row = 16 * c.slice + ((lane >> 1) & 15);
-  const uint32_t off = (uint32_t)row * rowbytes + (uint32_t)(lane & 1) * (D == 128 ? 128u : 64u);
-  dma16(rsrc(c.q + row0 * D, bytes), off, sink);
-  dma16(rsrc(c.k + row0 * D, bytes), off, sink);
-  dma16(rsrc(c.v + row0 * D, bytes), off, sink);
+  const uint32_t off = row_off(br, row, rowbytes) + (uint32_t)(lane & 1) * (D == 128 ? 128u : 64u);
+  if constexpr (!SO) dma16(rsrc(c.q + br.row0 * D, bytes), off, sink);
+  dma16(rsrc(c.k + br.row0 * D, bytes), off, sink);
+  dma16(rsrc(c.v + br.row0 * D, bytes), off, sink);
 }
-constexpr int PF_DMA = 3;   // prefetch instructions per block
+// prefetch instructions per block (no Q when only the state is computed)
+template <bool SO>
+constexpr int pf_dma() { return SO ? 2 : 3; }
 constexpr int PF_AHEAD = 4; // blocks between a block's prefetch and its DMA
 
 // ------------------------------------------------------------------------------------------
@@ -248,17 +264,20 @@ constexpr int PF_AHEAD = 4; // blocks between a block's prefetch and its DMA
 // decayed, lambda^(b-1-j) V[j], to the double-buffered copy the state waves consume (so no state
 // wave scales operands).
 // ------------------------------------------------------------------------------------------
-template <int D, int R>
+template <int D, int R, bool SO>
 __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const float *pw,
                                             int lane) {
   using C = Cfg<D>;
   constexpr int NT = R + 1;         // causal score tiles
   constexpr int NS = (NT + 1) / 2;  // 32-token k-steps of the intra product
-  // DMA instructions this wave issues per block.
-  constexpr int DMA = R == 0 ? C::QK_DMA + 2 : R == 1 ? 2 * C::QK_DMA + 1 : R == 2 ? C::QK_DMA + 1 : 0;
   // 16-row groups of V this wave loads and decays: [VG0, VG0 + NVG).
   constexpr int VG0 = R == 0 ? 0 : R == 1 ? 2 : 3;
   constexpr int NVG = R == 0 ? 2 : R == 3 ? 0 : 1;
+  // DMA instructions this wave issues per block (Q rows, none when only the state is computed,
+  // then its V groups) and output stores per block.
+  constexpr int QDMA = SO ? 0 : R == 1 ? 2 * C::QK_DMA : R < 3 ? C::QK_DMA : 0;
+  constexpr int DMA = QDMA + NVG;
+  constexpr int STORES = SO ? 0 : 2;
   const int l16 = lane & 15, g = lane >> 4;
   const int jrow = 16 * R + l16;  // this lane's output row inside a block
   const uint32_t smem_lds = lds_addr(smem);
@@ -276,6 +295,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       if (t == R) keep[i] = jp <= jrow;
     }
   const float inter_scale = pw[jrow + 1];
+  // Block 0 applies the initial state; weighted lambda^j instead when it counts as inclusive.
+  const float inter_first = c.incl ? pw[jrow] : inter_scale;
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
   const uint32_t rowbytes = (uint32_t)c.H * D * 2;
   // This wave's share of the decayed V copy: lane bytes 16 (lane % 4) .. +15 of V rows
@@ -291,8 +312,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 
   auto issue = [&](int blk) {
     const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
-    if constexpr (R < 3) dma_rows<D>(c.q, c, blk, R, st + C::Q_OFF, lane);
-    if constexpr (R == 1) dma_rows<D>(c.q, c, blk, 3, st + C::Q_OFF, lane);
+    if constexpr (!SO && R < 3) dma_rows<D>(c.q, c, blk, R, st + C::Q_OFF, lane);
+    if constexpr (!SO && R == 1) dma_rows<D>(c.q, c, blk, 3, st + C::Q_OFF, lane);
 #pragma unroll
     for (int m = 0; m < NVG; ++m) dma_vrows<D>(c, blk, VG0 + m, st + C::V_OFF, lane);
   };
@@ -320,91 +341,92 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 
   for (int i = 0; i < c.nb; ++i) {
     issue(i + NST - 1);  // refills the stage read in step i-1
-    const char *stage = smem + (i % NST) * C::STAGE;
-    const char *Qs = stage + C::Q_OFF;
-    const char *Ks = stage + C::K_OFF;
-    const char *Vs = stage + C::V_OFF;
-    const char *KVs = smem + C::KVX_OFF + (i & 1) * C::KVX;
+    if constexpr (!SO) {
+      const char *stage = smem + (i % NST) * C::STAGE;
+      const char *Qs = stage + C::Q_OFF;
+      const char *Ks = stage + C::K_OFF;
+      const char *Vs = stage + C::V_OFF;
+      const char *KVs = smem + C::KVX_OFF + (i & 1) * C::KVX;
 
-    // Q operand (B of S^T and of the inter product): Q[jrow][32 ks + 8 g + 0..7].
-    bf16x8 qop[C::KSTEPS];
+      // Q operand (B of S^T and of the inter product): Q[jrow][32 ks + 8 g + 0..7].
+      bf16x8 qop[C::KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks)
-      qop[ks] = *(const bf16x8 *)(Qs + swz<D>(jrow, 32 * ks + 8 * g));
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
+        qop[ks] = *(const bf16x8 *)(Qs + swz<D>(jrow, 32 * ks + 8 * g));
 
-    // S^T[16t + 4g + i][jrow] = P[jrow][16t + 4g + i] before masking.
-    f32x4 sacc[NT];
+      // S^T[16t + 4g + i][jrow] = P[jrow][16t + 4g + i] before masking.
+      f32x4 sacc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks)
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        sacc[t] = mfma(*(const bf16x8 *)(Ks + swz<D>(16 * t + l16, 32 * ks + 8 * g)), qop[ks],
-                       sacc[t]);
+        for (int t = 0; t < NT; ++t)
+          sacc[t] = mfma(*(const bf16x8 *)(Ks + swz<D>(16 * t + l16, 32 * ks + 8 * g)), qop[ks],
+                         sacc[t]);
 
-    // Inter part: O^T[16ct + 4g + i][jrow] = sum_dk KV[dk][16ct + 4g + i] Q[jrow][dk].
-    f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // Inter part: O^T[16ct + 4g + i][jrow] = sum_dk KV[dk][16ct + 4g + i] Q[jrow][dk].
+      f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks)
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        o[ct] = mfma(*(const bf16x8 *)(KVs + swz<D>(16 * ct + l16, 32 * ks + 8 * g)), qop[ks],
-                     o[ct]);
+        for (int ct = 0; ct < 2; ++ct)
+          o[ct] = mfma(*(const bf16x8 *)(KVs + swz<D>(16 * ct + l16, 32 * ks + 8 * g)), qop[ks],
+                       o[ct]);
 
-    // V operands of the causal k-steps: lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
-    bf16x8 vop[NS][2];
+      // V operands of the causal k-steps: lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
+      bf16x8 vop[NS][2];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROWB + 2 * (16 * ct + tcol));
-        const bf16x4 hi = tr_read(Vs + (32 * s + 16 + trow) * C::VROWB + 2 * (16 * ct + tcol));
-        vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int ct = 0; ct < 2; ++ct) {
+          const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROWB + 2 * (16 * ct + tcol));
+          const bf16x4 hi = tr_read(Vs + (32 * s + 16 + trow) * C::VROWB + 2 * (16 * ct + tcol));
+          vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+
+      // Decay/causal mask in registers, then P in bf16 (tiles past the diagonal are zero).
+      bf16x4 p[2 * NS];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 m = sacc[t] * f32x4{maskw[t][0], maskw[t][1], maskw[t][2], maskw[t][3]};
+        if (t == R) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m[e] = keep[e] ? m[e] : 0.f;
+        }
+        p[t] = to_bf16x4(m);
+      }
+      if constexpr (NT % 2) p[NT] = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+
+      // O^T = lambda^(j+1) * inter + V^T P^T.
+      const float isc = i == 0 ? inter_first : inter_scale;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) o[ct] *= isc;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 pop = __builtin_shufflevector(p[2 * s], p[2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) o[ct] = mfma(vop[s][ct], pop, o[ct]);
       }
 
-    // Decay/causal mask in registers, then P in bf16 (tiles past the diagonal are zero).
-    bf16x4 p[2 * NS];
+      // Store: lane holds O[jrow][c0 + 16ct + 4g + 0..3]; rows past the end are dropped.
+      {
+        const BlockRows br = block_rows(c, i);
+        const auto ro = rsrc(c.out + br.row0 * D + c.c0, (uint32_t)br.b * rowbytes);
+        const uint32_t off = row_off(br, jrow, rowbytes) + 8u * g;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 m = sacc[t] * f32x4{maskw[t][0], maskw[t][1], maskw[t][2], maskw[t][3]};
-      if (t == R) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m[e] = keep[e] ? m[e] : 0.f;
+        for (int ct = 0; ct < 2; ++ct)
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(o[ct])), ro,
+                                                off + 32u * ct, 0, 0);
       }
-      p[t] = to_bf16x4(m);
-    }
-    if constexpr (NT % 2) p[NT] = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-
-    // O^T = lambda^(j+1) * inter + V^T P^T.
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) o[ct] *= inter_scale;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 pop = __builtin_shufflevector(p[2 * s], p[2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) o[ct] = mfma(vop[s][ct], pop, o[ct]);
-    }
-
-    // Store: lane holds O[jrow][c0 + 16ct + 4g + 0..3]; rows past the end are dropped.
-    {
-      const int64_t rem = c.n - (int64_t)i * BLK;
-      const int b = rem < BLK ? (int)rem : BLK;
-      const int64_t row0 = (c.tok0 + (int64_t)i * BLK) * c.H + c.h;
-      const auto ro = rsrc(c.out + row0 * D + c.c0, (uint32_t)b * rowbytes);
-      const uint32_t off = (uint32_t)jrow * rowbytes + 8u * g;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(o[ct])), ro,
-                                              off + 32u * ct, 0, 0);
-    }
+    }  // !SO
 
     // Own rows of block i+1 landed: its DMA was issued in step i-1 (or the prologue); since
-    // then this wave issued that step's 2 stores, this step's DMA and 2 stores.
+    // then this wave issued that step's stores, this step's DMA and stores.
     static_assert(NST == 3, "wait counts are written for three stages");
     if constexpr (DMA > 0) {
-      if (i == 0) wait_vm<DMA + 2>();
-      else wait_vm<DMA + 4>();
+      if (i == 0) wait_vm<DMA + STORES>();
+      else wait_vm<DMA + 2 * STORES>();
     }
     decay_v(i + 1);
     lds_barrier();
@@ -416,7 +438,7 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 // State wave r: its band of the fp32 state.  Issues the DMA of K rows 16r..16r+15; the lightest
 // state wave (r = 3) also issues the L2 prefetches.
 // ------------------------------------------------------------------------------------------
-template <int D, int R>
+template <int D, int R, bool SO>
 __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const float *pw,
                                            const float *s0, float *fs, size_t sbase, int lane) {
   using C = Cfg<D>;
@@ -424,6 +446,7 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   constexpr int RT = Bd::RT;
   constexpr int DK0 = Bd::DK0;
   constexpr bool PF = R == 3;
+  constexpr int PF_DMA = pf_dma<SO>();
   constexpr int DMA = C::QK_DMA + (PF ? PF_DMA : 0);
   // Operations issued after a block's K DMA until the wait for it: the NST-2 later issues, plus,
   // with prefetches (issued after the K DMA of the same block), that block's own prefetches.
@@ -440,7 +463,7 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
-        kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
+        kv[rt][ct][i] = s0 ? s0[sbase + (c.s0t ? (size_t)dv * D + dk : (size_t)dk * D + dv)] : 0.f;
       }
   auto write_kvx = [&](char *dst) {
 #pragma unroll
@@ -454,6 +477,9 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   // lambda^b for full blocks and for the last block, which may be partial (b_last rows).
   const int b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
   const float lb_full = pw[BLK], lb_last = pw[b_last];
+  // Block 0 decays the initial state by lambda^(b0 - 1) when it counts as inclusive.
+  const int b0 = c.nb == 1 ? b_last : BLK;
+  const float lb_first = c.incl ? pw[b0 - 1] : pw[b0];
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
 
   auto issue = [&](int blk) {
@@ -461,12 +487,12 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
     dma_rows<D>(c.k, c, blk, R, st + C::K_OFF, lane);
     // after the DMA, so that waiting for this DMA never waits for a prefetch (counters are
     // in order)
-    if constexpr (PF) prefetch_l2<D>(c, blk + PF_AHEAD, smem_lds + C::PF_OFF, lane);
+    if constexpr (PF) prefetch_l2<D, SO>(c, blk + PF_AHEAD, smem_lds + C::PF_OFF, lane);
   };
   if constexpr (PF) {
     // Blocks NST-1 .. PF_AHEAD-1 are not covered by the prefetches of the first issues.
     for (int blk = NST - 1; blk < PF_AHEAD; ++blk)
-      prefetch_l2<D>(c, blk, smem_lds + C::PF_OFF, lane);
+      prefetch_l2<D, SO>(c, blk, smem_lds + C::PF_OFF, lane);
   }
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s);
@@ -477,7 +503,7 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
     const char *Ks = smem + (i % NST) * C::STAGE + C::K_OFF;
     const char *LVs = smem + C::LV_OFF + (i & 1) * C::LV;  // lambda^(b-1-j) V[j]
     if constexpr (RT > 0) {
-      const float lb = i == c.nb - 1 ? lb_last : lb_full;
+      const float lb = i == 0 ? lb_first : i == c.nb - 1 ? lb_last : lb_full;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -509,6 +535,7 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (fs) {
+    const float fsc = c.incl && c.nb > 0 ? pw[1] : 1.f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -516,17 +543,19 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
-          fs[sbase + (size_t)dk * D + dv] = kv[rt][ct][i];
+          fs[sbase + (size_t)dk * D + dv] = kv[rt][ct][i] * fsc;
         }
   }
 }
 
-template <int D>
+// flags: bit 0 reversed scan, bit 1 inclusive initial state, bit 2 transposed initial state.
+// SO: compute only the final state (q and out are not touched).
+template <int D, bool SO>
 __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, __bf16 *__restrict__ out, float *__restrict__ fs, int64_t T,
-    int S, int H) {
+    int S, int H, int flags) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -560,6 +589,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   c.h = h;
   c.c0 = slice * CV;
   c.slice = slice;
+  c.rev = flags & 1;
+  c.incl = flags & 2;
+  c.s0t = flags & 4;
 
   const int tid = threadIdx.x;
   // Zero the stages once: rows a partial block does not load then hold zeros or finite values
@@ -577,31 +609,33 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   const int lane = tid & 63;
   switch (tid >> 6) {
-    case 0: output_wave<D, 0>(c, smem, pw, lane); break;
-    case 1: output_wave<D, 1>(c, smem, pw, lane); break;
-    case 2: output_wave<D, 2>(c, smem, pw, lane); break;
-    case 3: output_wave<D, 3>(c, smem, pw, lane); break;
-    case 4: state_wave<D, 0>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 5: state_wave<D, 1>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 6: state_wave<D, 2>(c, smem, pw, s0, fs, sbase, lane); break;
-    default: state_wave<D, 3>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 0: output_wave<D, 0, SO>(c, smem, pw, lane); break;
+    case 1: output_wave<D, 1, SO>(c, smem, pw, lane); break;
+    case 2: output_wave<D, 2, SO>(c, smem, pw, lane); break;
+    case 3: output_wave<D, 3, SO>(c, smem, pw, lane); break;
+    case 4: state_wave<D, 0, SO>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 5: state_wave<D, 1, SO>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 6: state_wave<D, 2, SO>(c, smem, pw, s0, fs, sbase, lane); break;
+    default: state_wave<D, 3, SO>(c, smem, pw, s0, fs, sbase, lane); break;
   }
 }
 
-template <int D>
+template <int D, bool SO>
 hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   const int NS = D / CV;
   const long long grid = (long long)a.S * a.H * NS;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)grid), dim3(NTHR), 0, stream,
+  const int flags = (a.reverse ? 1 : 0) | (a.init_inclusive ? 2 : 0) | (a.init_transposed ? 4 : 0);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, SO>), dim3((unsigned)grid), dim3(NTHR), 0, stream,
                      (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, a.decay,
                      a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state, a.T, a.S,
-                     a.H);
+                     a.H, flags);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t la_launch_prefill_bf16(const LaPrefillArgs &a, hipStream_t stream) {
-  return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
+  if (a.state_only) return a.D == 128 ? launch<128, true>(a, stream) : launch<64, true>(a, stream);
+  return a.D == 128 ? launch<128, false>(a, stream) : launch<64, false>(a, stream);
 }

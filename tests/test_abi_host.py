@@ -110,3 +110,41 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(8, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         la.prefill(q, q, q.to(torch.float32), torch.ones(1))
+
+
+def _split(lib, seg_blocks=4, ws=ctypes.c_void_p(0x300000), ws_bytes=1 << 30, T=1000, S=1, H=2,
+           D=128, cu=None, init=None, fs=None, q=P):
+    return lib.la_prefill_split(q, P, P, P, cu, init, P2, fs, T, S, H, D, 1, seg_blocks, ws,
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(seg_blocks=0), dict(seg_blocks=-2), dict(ws=None), dict(ws=ctypes.c_void_p(0x300010)),
+    dict(ws_bytes=1000), dict(T=1 << 31), dict(S=0), dict(S=3), dict(init=P2, fs=P2),
+    dict(q=None),
+])
+def test_split_validation(lib, kwargs):
+    assert _split(lib, **kwargs) == 1
+    assert lib.la_last_error() != b""
+
+
+def test_split_workspace_size(lib):
+    def expect(T, S, H, D, nb):
+        a = lambda x: (x + 255) // 256 * 256
+        cap = -(-T // (64 * nb)) + S - 1 if T > 0 else 0
+        return a(cap * H * D * D * 4) + a((cap + 1) * 4) + a((S + 1) * 4)
+
+    for args in [(8192, 1, 8, 128, 16), (1000, 3, 2, 64, 1), (1, 1, 1, 128, 7), (0, 2, 4, 64, 2),
+                 (272568, 16, 64, 128, 64)]:
+        assert lib.la_prefill_split_workspace_size(*args) == expect(*args), args
+    assert lib.la_prefill_split_workspace_size(100, 1, 1, 96, 4) == 0
+    assert lib.la_prefill_split_workspace_size(100, 1, 1, 128, 0) == 0
+
+
+def test_split_without_device(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert lib.la_prefill_split_blocks(8192, 1, 8, 128) == 0
+    assert _split(lib) == 3

@@ -1,0 +1,97 @@
+"""GPU parity of the sequence-split prefill (segments scanned in parallel, then combined) against
+the fp64 oracle, and against the plain prefill.
+
+Segment lengths of 1 and 2 blocks put segment boundaries inside every sequence of the ragged
+batch, next to empty sequences and partial last blocks; the 8k x 8 and 64k x 8 cases are the
+few-chain shapes the split exists for.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_attn_amd as la
+import oracle
+from gpu_util import BF16_TOL, F32_TOL, banner, dev, slice_errors, state_errors, to_np
+from long_context_attention_attn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: BF16_TOL, torch.float32: F32_TOL}
+RAGGED = [1, 63, 64, 65, 0, 130, 200, 7]
+
+
+def _split_prefill(q, k, v, decay, cu=None, init=None, split=None):
+    d = dev()
+    out, fs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d), None if cu is None else cu.to(d),
+                         initial_state=None if init is None else init.to(d), split=split)
+    torch.cuda.synchronize()
+    return out, fs
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("with_init", [False, True], ids=["zero_state", "init_state"])
+@pytest.mark.parametrize("seg_blocks", [1, 2])
+def test_split_ragged_varlen(dtype, D, with_init, seg_blocks):
+    banner("split ragged dtype=%s D=%d init=%s seg_blocks=%d" % (dtype, D, with_init, seg_blocks))
+    H = 3
+    cu = synth.cu_from_lengths(RAGGED)
+    q, k, v = synth.qkv(int(cu[-1]), H, D, dtype, seed=3)
+    decay = torch.tensor([0.0, 0.95, 1.0], dtype=torch.float32)
+    init = synth.random_state(len(RAGGED), H, D, seed=4, scale=0.1) if with_init else None
+    out, fs = _split_prefill(q, k, v, decay, cu, init, split=seg_blocks)
+    ref = oracle.quadratic(q, k, v, decay, cu, init_state=init)
+    ref_s = oracle.final_state(k, v, decay, cu, init_state=init)
+    e = slice_errors(to_np(out), ref, cu)
+    es = state_errors(to_np(fs), ref_s)
+    print("split ragged: max out %.2e max state %.2e" % (e.max(), es.max()))
+    assert e.max() <= TOL[dtype] and es.max() <= TOL[dtype]
+    if not with_init:
+        assert torch.count_nonzero(fs[4]).item() == 0
+    else:
+        assert torch.equal(fs[4].cpu(), init[4])
+
+
+def test_split_8k_full_quadratic():
+    """8 heads x 8,192 tokens (32 workgroups unsplit): split into 16-block segments and 'auto',
+    every row against the quadratic oracle."""
+    wl = synth.workloads()["prefill_8k"]
+    banner("split prefill_8k T=8192 H=8 D=128 bf16")
+    q, k, v = wl.inputs()
+    decay = wl.decay()
+    ref = oracle.quadratic(q, k, v, decay)
+    ref_s = oracle.final_state(k, v, decay)
+    for split in (16, "auto"):
+        out, fs = _split_prefill(q, k, v, decay, split=split)
+        e = slice_errors(to_np(out), ref, [0, wl.T])
+        es = state_errors(to_np(fs), ref_s)
+        print("split=%s: out %.2e state %.2e" % (split, e.max(), es.max()))
+        assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
+
+
+def test_split_matches_plain_and_is_deterministic():
+    banner("split vs plain T=5000 H=4 D=128 bf16")
+    q, k, v = synth.qkv(5000, 4, 128, torch.bfloat16, seed=21)
+    decay = synth.decay_geometric(4, 0.9, 0.9999)
+    o1, s1 = _split_prefill(q, k, v, decay, split=3)
+    o2, s2 = _split_prefill(q, k, v, decay, split=3)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    op, sp = _split_prefill(q, k, v, decay)
+    assert slice_errors(to_np(o1), to_np(op), [0, 5000]).max() <= BF16_TOL
+    assert state_errors(to_np(s1), to_np(sp)).max() <= BF16_TOL
+
+
+def test_split_64k_8_heads_recurrent():
+    """65,536 tokens x 8 heads (one device's share of the 64-head layer under 8-way head
+    sharding): 'auto' split, all heads against the recurrent oracle."""
+    banner("split T=65536 H=8 D=128 bf16 auto")
+    T, H, D = 65536, 8, 128
+    q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=0)
+    decay = synth.decay_geometric(H, 0.9, 0.9999)
+    out, fs = _split_prefill(q, k, v, decay, split="auto")
+    ref, ref_s = oracle.recurrent(q, k, v, decay)
+    e = slice_errors(to_np(out), ref, [0, T])
+    es = state_errors(to_np(fs), ref_s)
+    print("split 64k x 8: out", np.array2string(e[0], formatter={"float_kind": lambda x: "%.2e" % x}),
+          "state max %.2e" % es.max())
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
