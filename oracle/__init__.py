@@ -15,6 +15,9 @@ Functions (all inputs are converted to contiguous float64; layouts [T, H, D] and
 * ``final_state``     -- O3, closed form sum_s lambda^(n-1-s) k_s^T v_s (+ lambda^n S0).
 * ``decode_step``     -- O4, one recurrent step for a batch of states.
 * ``unmasked_left`` / ``unmasked_right`` -- O5, (Q K^T) V and Q (K^T V) for one head.
+* ``backward``        -- O6, gradients dq, dk, dv, dS0 of the prefill, term by term from the
+  derivative of the definition (quadratic in n).
+* ``backward_recurrent`` -- O7, the same gradients through a forward and a reverse state scan.
 
 The definitions follow the pages' statement of causal linear attention and its association
 orders (MiniMax-01 technical-report digest on futurefh.com, section 1; nabfollower blog,
@@ -63,10 +66,13 @@ def _bind(lib):
     lib.lao_decode_step.argtypes = [_DP, _DP, _DP, _DP, i32, i32, i32, _DP, _DP]
     lib.lao_unmasked_left.argtypes = [_DP, _DP, _DP, i64, i32, _DP]
     lib.lao_unmasked_right.argtypes = [_DP, _DP, _DP, i64, i32, _DP]
+    for name in ("lao_backward", "lao_backward_recurrent"):
+        getattr(lib, name).argtypes = [_DP, _DP, _DP, _DP, _IP, i32, i64, i32, i32, _DP, _DP, _DP,
+                                       _DP, _DP, _DP, _DP]
     lib.lao_num_threads.argtypes = []
     for name in ("lao_quadratic", "lao_quadratic_rows", "lao_recurrent", "lao_final_state",
                  "lao_decode_step", "lao_unmasked_left", "lao_unmasked_right",
-                 "lao_num_threads"):
+                 "lao_backward", "lao_backward_recurrent", "lao_num_threads"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -189,6 +195,32 @@ class Oracle:
                "unmasked_right")
         return out
 
+    def _bwd(self, fn, q, k, v, decay, d_out, cu_seqlens, init_state, d_final, want_d_init):
+        q, k, v, decay, d_out, init_state, d_final = map(
+            _f64, (q, k, v, decay, d_out, init_state, d_final))
+        cu = _i32(cu_seqlens)
+        S, T, H, D = _shape(q, cu)
+        dq, dk, dv = (np.zeros((T, H, D), np.float64) for _ in range(3))
+        di = np.zeros((S, H, D, D), np.float64) if want_d_init else None
+        rc = getattr(self.lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu, _IP), S, T,
+                                   H, D, _ptr(init_state), _ptr(d_out), _ptr(d_final), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(di))
+        _check(rc, fn)
+        return dq, dk, dv, di
+
+    def backward(self, q, k, v, decay, d_out, cu_seqlens=None, init_state=None, d_final=None,
+                 want_d_init=True):
+        """O6 -> (dq, dk, dv [T,H,D], d_init [S,H,D,D] or None) for upstream gradients d_out
+        [T,H,D] and d_final [S,H,D,D] (None = 0)."""
+        return self._bwd("lao_backward", q, k, v, decay, d_out, cu_seqlens, init_state, d_final,
+                         want_d_init)
+
+    def backward_recurrent(self, q, k, v, decay, d_out, cu_seqlens=None, init_state=None,
+                           d_final=None, want_d_init=True):
+        """O7: the gradients of ``backward`` through a forward and a reverse state scan."""
+        return self._bwd("lao_backward_recurrent", q, k, v, decay, d_out, cu_seqlens, init_state,
+                         d_final, want_d_init)
+
     def num_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.lao_num_threads())
@@ -234,6 +266,14 @@ def unmasked_left(*a, **kw):
 
 def unmasked_right(*a, **kw):
     return default().unmasked_right(*a, **kw)
+
+
+def backward(*a, **kw):
+    return default().backward(*a, **kw)
+
+
+def backward_recurrent(*a, **kw):
+    return default().backward_recurrent(*a, **kw)
 
 
 def num_threads() -> int:

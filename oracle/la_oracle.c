@@ -277,6 +277,193 @@ int lao_unmasked_right(const double *q, const double *k, const double *v, int64_
   return 0;
 }
 
+/* O6.  Each gradient row is its own sum over the other time index, written as in the
+ * definition: dq_t over s <= t, dk_s and dv_s over t >= s, dS0 over all t. */
+int lao_backward(const double *q, const double *k, const double *v, const double *decay,
+                 const int32_t *cu_seqlens, int32_t S, int64_t T, int32_t H, int32_t D,
+                 const double *init_state, const double *d_out, const double *d_final,
+                 double *dq, double *dk, double *dv, double *d_init) {
+  if (q == NULL || k == NULL || v == NULL || d_out == NULL || dq == NULL || dk == NULL ||
+      dv == NULL)
+    return -1;
+  if (check_common(decay, cu_seqlens, S, T, H, D) != 0) return -1;
+  for (int32_t sq = 0; sq < S; ++sq) {
+    int64_t beg, end;
+    seq_bounds(cu_seqlens, T, sq, &beg, &end);
+    const int64_t n = end - beg;
+#pragma omp parallel for collapse(2) schedule(dynamic, 8)
+    for (int64_t i = 0; i < n; ++i) {
+      for (int32_t h = 0; h < H; ++h) {
+        const double lam = decay[h];
+        const double *S0 = init_state ? init_state + state_off(sq, h, H, D) : NULL;
+        const double *dSn = d_final ? d_final + state_off(sq, h, H, D) : NULL;
+        const int64_t t = beg + i; /* this row's token */
+        /* dq_t = sum_{s<=t} lambda^(t-s) (do_t . v_s) k_s + lambda^(t+1) S0 do_t */
+        {
+          const double *dout_t = d_out + act_off(t, h, H, D);
+          double *g = dq + act_off(t, h, H, D);
+          for (int32_t a = 0; a < D; ++a) g[a] = 0.0;
+          double w = 1.0; /* lambda^(t-s) */
+          for (int64_t s = t; s >= beg; --s) {
+            const double c = w * dot(dout_t, v + act_off(s, h, H, D), D);
+            const double *ks = k + act_off(s, h, H, D);
+            for (int32_t a = 0; a < D; ++a) g[a] += c * ks[a];
+            w *= lam;
+          }
+          if (S0 != NULL) /* w = lambda^(t-beg+1) */
+            for (int32_t a = 0; a < D; ++a) {
+              double acc = 0.0;
+              for (int32_t b = 0; b < D; ++b) acc += S0[(size_t)a * D + b] * dout_t[b];
+              g[a] += w * acc;
+            }
+        }
+        /* dk_t and dv_t (t in the role of s above): sums over t' >= t */
+        {
+          const double *kt = k + act_off(t, h, H, D);
+          const double *vt = v + act_off(t, h, H, D);
+          double *gk = dk + act_off(t, h, H, D);
+          double *gv = dv + act_off(t, h, H, D);
+          for (int32_t a = 0; a < D; ++a) gk[a] = gv[a] = 0.0;
+          double w = 1.0; /* lambda^(t'-t) */
+          for (int64_t tp = t; tp < end; ++tp) {
+            const double *qp = q + act_off(tp, h, H, D);
+            const double *dp = d_out + act_off(tp, h, H, D);
+            const double ck = w * dot(dp, vt, D);
+            const double cv = w * dot(qp, kt, D);
+            for (int32_t a = 0; a < D; ++a) {
+              gk[a] += ck * qp[a];
+              gv[a] += cv * dp[a];
+            }
+            w *= lam;
+          }
+          if (dSn != NULL) {
+            /* lambda^(end-1-t) = w / lambda would divide by zero at lambda = 0: recompute */
+            double wn = 1.0;
+            for (int64_t m = t; m < end - 1; ++m) wn *= lam;
+            for (int32_t a = 0; a < D; ++a) {
+              double acck = 0.0, accv = 0.0;
+              for (int32_t b = 0; b < D; ++b) {
+                acck += dSn[(size_t)a * D + b] * vt[b];
+                accv += dSn[(size_t)b * D + a] * kt[b];
+              }
+              gk[a] += wn * acck;
+              gv[a] += wn * accv;
+            }
+          }
+        }
+      }
+    }
+    if (d_init != NULL) {
+      /* dS0 = sum_t lambda^(t+1) q_t^T do_t + lambda^n dSn */
+#pragma omp parallel for schedule(dynamic, 1)
+      for (int32_t h = 0; h < H; ++h) {
+        const double lam = decay[h];
+        double *g = d_init + state_off(sq, h, H, D);
+        for (size_t e = 0; e < (size_t)D * D; ++e) g[e] = 0.0;
+        double w = lam; /* lambda^(t+1) at t = beg */
+        for (int64_t t = beg; t < end; ++t) {
+          const double *qt = q + act_off(t, h, H, D);
+          const double *dt = d_out + act_off(t, h, H, D);
+          for (int32_t a = 0; a < D; ++a)
+            for (int32_t b = 0; b < D; ++b) g[(size_t)a * D + b] += w * qt[a] * dt[b];
+          w *= lam;
+        }
+        if (d_final != NULL) {
+          double wn = 1.0;
+          for (int64_t m = 0; m < n; ++m) wn *= lam;
+          const double *dSn = d_final + state_off(sq, h, H, D);
+          for (size_t e = 0; e < (size_t)D * D; ++e) g[e] += wn * dSn[e];
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* O7.  Forward scan for dq, reverse scan for dk, dv and dS0. */
+int lao_backward_recurrent(const double *q, const double *k, const double *v,
+                           const double *decay, const int32_t *cu_seqlens, int32_t S, int64_t T,
+                           int32_t H, int32_t D, const double *init_state, const double *d_out,
+                           const double *d_final, double *dq, double *dk, double *dv,
+                           double *d_init) {
+  if (q == NULL || k == NULL || v == NULL || d_out == NULL || dq == NULL || dk == NULL ||
+      dv == NULL)
+    return -1;
+  if (check_common(decay, cu_seqlens, S, T, H, D) != 0) return -1;
+  int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : bad)
+  for (int32_t sq = 0; sq < S; ++sq) {
+    for (int32_t h = 0; h < H; ++h) {
+      const size_t DD = (size_t)D * D;
+      double *St = (double *)malloc(sizeof(double) * DD);
+      double *G = (double *)malloc(sizeof(double) * DD);
+      if (St == NULL || G == NULL) {
+        free(St);
+        free(G);
+        bad |= 1;
+        continue;
+      }
+      const double lam = decay[h];
+      int64_t beg, end;
+      seq_bounds(cu_seqlens, T, sq, &beg, &end);
+      /* forward: S_t = lambda S_{t-1} + k_t^T v_t, dq_t = S_t do_t */
+      if (init_state)
+        memcpy(St, init_state + state_off(sq, h, H, D), sizeof(double) * DD);
+      else
+        memset(St, 0, sizeof(double) * DD);
+      for (int64_t t = beg; t < end; ++t) {
+        const double *kt = k + act_off(t, h, H, D);
+        const double *vt = v + act_off(t, h, H, D);
+        const double *dt = d_out + act_off(t, h, H, D);
+        double *g = dq + act_off(t, h, H, D);
+        for (int32_t a = 0; a < D; ++a)
+          for (int32_t b = 0; b < D; ++b)
+            St[(size_t)a * D + b] = lam * St[(size_t)a * D + b] + kt[a] * vt[b];
+        for (int32_t a = 0; a < D; ++a) {
+          double acc = 0.0;
+          for (int32_t b = 0; b < D; ++b) acc += St[(size_t)a * D + b] * dt[b];
+          g[a] = acc;
+        }
+      }
+      /* reverse: G starts as dSn; G_t = lambda G_{t+1} + q_t^T do_t (no decay before the
+       * last token's term), dk_t = G_t v_t, dv_t = G_t^T k_t */
+      if (d_final)
+        memcpy(G, d_final + state_off(sq, h, H, D), sizeof(double) * DD);
+      else
+        memset(G, 0, sizeof(double) * DD);
+      for (int64_t t = end - 1; t >= beg; --t) {
+        const double *qt = q + act_off(t, h, H, D);
+        const double *kt = k + act_off(t, h, H, D);
+        const double *vt = v + act_off(t, h, H, D);
+        const double *dt = d_out + act_off(t, h, H, D);
+        const double w = t == end - 1 ? 1.0 : lam;
+        for (int32_t a = 0; a < D; ++a)
+          for (int32_t b = 0; b < D; ++b)
+            G[(size_t)a * D + b] = w * G[(size_t)a * D + b] + qt[a] * dt[b];
+        double *gk = dk + act_off(t, h, H, D);
+        double *gv = dv + act_off(t, h, H, D);
+        for (int32_t a = 0; a < D; ++a) {
+          double acck = 0.0, accv = 0.0;
+          for (int32_t b = 0; b < D; ++b) {
+            acck += G[(size_t)a * D + b] * vt[b];
+            accv += G[(size_t)b * D + a] * kt[b];
+          }
+          gk[a] = acck;
+          gv[a] = accv;
+        }
+      }
+      if (d_init != NULL) {
+        double *g = d_init + state_off(sq, h, H, D);
+        const double w = end > beg ? lam : 1.0;
+        for (size_t e = 0; e < DD; ++e) g[e] = w * G[e];
+      }
+      free(St);
+      free(G);
+    }
+  }
+  return bad ? -1 : 0;
+}
+
 int lao_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -77,6 +77,38 @@ int lao_unmasked_left(const double *q, const double *k, const double *v, int64_t
 int lao_unmasked_right(const double *q, const double *k, const double *v, int64_t n, int32_t D,
                        double *out);
 
+/*
+ * Gradients of the prefill.  The pages give no backward pass (they state only that the model
+ * trains at up to a million tokens of context, abstract of the MiniMax-01 report, and that the
+ * training framework parallelises lightning attention over the sequence, technical-report
+ * digest section 2); what follows is the derivative of the definition above.  For a loss L with
+ * dL/do_t = do_t and dL/dfinal_state = dSn (per sequence and head, dSn may be absent = 0):
+ *
+ *   dq_t  = sum_{s<=t} lambda^(t-s) (do_t . v_s) k_s  +  lambda^(t+1) S0 do_t
+ *   dk_s  = sum_{t>=s} lambda^(t-s) (do_t . v_s) q_t  +  lambda^(n-1-s) dSn v_s
+ *   dv_s  = sum_{t>=s} lambda^(t-s) (q_t . k_s) do_t  +  lambda^(n-1-s) dSn^T k_s
+ *   dS0   = sum_t lambda^(t+1) q_t^T do_t  +  lambda^n dSn
+ *
+ * (S0 do_t is the vector sum_b S0[a][b] do_t[b]; dSn v_s likewise; dSn^T k_s is
+ * sum_a dSn[a][b] k_s[a].)  lambda is a constant of the operation; no gradient for it.
+ *
+ * O6: the sums above, term by term (quadratic in n).  O7: the same through two scans:
+ *   forward  S_t = lambda S_{t-1} + k_t^T v_t (S_{-1} = S0),  dq_t = S_t do_t;
+ *   backward G_t = lambda G_{t+1} + q_t^T do_t (G_{n-1} = q^T do + dSn),
+ *            dk_s = G_s v_s,  dv_s = G_s^T k_s,  dS0 = lambda G_0 (dSn when n = 0).
+ * init_state and d_final may be NULL (zeros); d_init may be NULL (not computed).
+ * dq, dk, dv: [T][H][D]; d_init: [S][H][D][D].
+ */
+int lao_backward(const double *q, const double *k, const double *v, const double *decay,
+                 const int32_t *cu_seqlens, int32_t S, int64_t T, int32_t H, int32_t D,
+                 const double *init_state, const double *d_out, const double *d_final,
+                 double *dq, double *dk, double *dv, double *d_init);
+int lao_backward_recurrent(const double *q, const double *k, const double *v,
+                           const double *decay, const int32_t *cu_seqlens, int32_t S, int64_t T,
+                           int32_t H, int32_t D, const double *init_state, const double *d_out,
+                           const double *d_final, double *dq, double *dk, double *dv,
+                           double *d_init);
+
 /* Number of OpenMP threads a parallel region of this library uses (1 without OpenMP). */
 int lao_num_threads(void);
 

@@ -29,15 +29,29 @@ def case():
     return q, k, v, np.array(DECAY), cu, S0
 
 
+def backward_case():
+    """case() plus upstream gradients d_out [T,H,D] and d_final [S,H,D,D], drawn after it."""
+    rng = np.random.default_rng(SEED)
+    T = sum(LENGTHS)
+    for _ in range(3):
+        rng.standard_normal((T, H, D))
+    rng.standard_normal((len(LENGTHS), H, D, D))
+    d_out = rng.standard_normal((T, H, D))
+    d_final = rng.standard_normal((len(LENGTHS), H, D, D))
+    return case() + (d_out, d_final)
+
+
 def main():
-    q, k, v, lam, cu, S0 = case()
+    q, k, v, lam, cu, S0, d_out, d_final = backward_case()
     out = oracle.quadratic(q, k, v, lam, cu, init_state=S0)
     st = oracle.final_state(k, v, lam, cu, init_state=S0)
+    dq, dk, dv, d_init = oracle.backward(q, k, v, lam, d_out, cu, init_state=S0, d_final=d_final)
     doc = {
         "what": "fp64 oracle outputs for a seeded varlen case with an empty sequence and an "
                 "initial state; written by tests/golden/make_golden.py from the oracle only",
         "lengths": LENGTHS, "H": H, "D": D, "seed": SEED, "decay": DECAY,
         "out": out.tolist(), "final_state": st.tolist(),
+        "dq": dq.tolist(), "dk": dk.tolist(), "dv": dv.tolist(), "d_init": d_init.tolist(),
     }
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_regression.json")
     with open(path, "w") as f:

@@ -310,6 +310,159 @@ def pin_block_form(o):
             close(KV, want_s, TOL, "block form state lam=%g B=%d" % (lam, B))
 
 
+# --------------------------------------------------------------------------------------------
+# Backward pins.  The gradients are those of L = <do, o> + <dSn, final_state>; L is linear in
+# each of q, k, v and S0 separately, so a central difference of the (already pinned) forward
+# oracle is exact up to rounding, for any step.
+# --------------------------------------------------------------------------------------------
+def _loss(o, q, k, v, lams, cu, S0, do, dSn):
+    return float(np.sum(do * o.quadratic(q, k, v, lams, cu, init_state=S0)) +
+                 np.sum(dSn * o.final_state(k, v, lams, cu, init_state=S0)))
+
+
+def _bwd_case(seed):
+    """Packed lengths 3, 0, 4 (an empty sequence), H=3 heads with lambda 0, 0.6, 1, D=3."""
+    lengths = [3, 0, 4]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H, D, S = int(cu[-1]), 3, 3, len(lengths)
+    lams = np.array([0.0, 0.6, 1.0])
+    q, k, v, do = (rnd((T, H, D), seed + i) for i in range(4))
+    S0, dSn = rnd((S, H, D, D), seed + 4), rnd((S, H, D, D), seed + 5)
+    return q, k, v, lams, cu, S0, do, dSn
+
+
+def pin_backward_finite_difference(o):
+    """Every entry of dq, dk, dv, dS0 (both O6 and O7) equals the central difference of the
+    forward oracle's loss."""
+    q, k, v, lams, cu, S0, do, dSn = _bwd_case(40)
+    args = dict(q=q, k=k, v=v, S0=S0)
+    eps = 0.25
+    num = {}
+    for name, x in args.items():
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a = {n: (y.copy() if n == name else y) for n, y in args.items()}
+            a[name][idx] += eps
+            lp = _loss(o, a["q"], a["k"], a["v"], lams, cu, a["S0"], do, dSn)
+            a[name][idx] -= 2 * eps
+            lm = _loss(o, a["q"], a["k"], a["v"], lams, cu, a["S0"], do, dSn)
+            g[idx] = (lp - lm) / (2 * eps)
+        num[name] = g
+    for fn in (o.backward, o.backward_recurrent):
+        dq, dk, dv, dS0 = fn(q, k, v, lams, do, cu, init_state=S0, d_final=dSn)
+        close(dq, num["q"], 1e-12, "%s dq vs finite difference" % fn.__name__)
+        close(dk, num["k"], 1e-12, "%s dk vs finite difference" % fn.__name__)
+        close(dv, num["v"], 1e-12, "%s dv vs finite difference" % fn.__name__)
+        close(dS0, num["S0"], 1e-12, "%s dS0 vs finite difference" % fn.__name__)
+
+
+def pin_backward_autograd(o):
+    """torch autograd (fp64, CPU) through the explicit mask-matrix form
+    o = ((Q K^T) * Dm) V + diag(lambda^(t+1)) Q S0, final = K^T diag(lambda^(n-1-s)) V + lambda^n S0."""
+    import torch
+
+    n, D = 20, 5
+    lams = [0.0, 0.5, 0.95, 1.0]
+    H = len(lams)
+    q, k, v, do = (rnd((n, H, D), 50 + i) for i in range(4))
+    S0, dSn = rnd((1, H, D, D), 54), rnd((1, H, D, D), 55)
+    want = [np.zeros((n, H, D)) for _ in range(3)] + [np.zeros((1, H, D, D))]
+    t = torch.arange(n, dtype=torch.float64)
+    for h, lam in enumerate(lams):
+        Q, K, V, S = (torch.tensor(x[:, h] if x.ndim == 3 else x[0, h], requires_grad=True)
+                      for x in (q, k, v, S0))
+        diff = t[:, None] - t[None, :]
+        Dm = torch.where(diff >= 0, torch.tensor(lam, dtype=torch.float64) ** diff.clamp(min=0),
+                         torch.zeros((), dtype=torch.float64))
+        out = ((Q @ K.T) * Dm) @ V + (lam ** (t + 1))[:, None] * (Q @ S)
+        fin = K.T @ ((lam ** (n - 1 - t))[:, None] * V) + lam ** n * S
+        L = (out * torch.tensor(do[:, h])).sum() + (fin * torch.tensor(dSn[0, h])).sum()
+        gq, gk, gv, gs = torch.autograd.grad(L, (Q, K, V, S))
+        want[0][:, h], want[1][:, h], want[2][:, h], want[3][0, h] = (
+            gq.numpy(), gk.numpy(), gv.numpy(), gs.numpy())
+    for fn in (o.backward, o.backward_recurrent):
+        got = fn(q, k, v, np.array(lams), do, init_state=S0, d_final=dSn)
+        for name, g, w in zip(("dq", "dk", "dv", "dS0"), got, want):
+            close(g, w, 1e-12, "%s %s vs autograd" % (fn.__name__, name))
+
+
+def pin_backward_lambda_zero(o):
+    """lambda = 0: o_t = (q_t . k_t) v_t and final = k_{n-1}^T v_{n-1}, so dq_t = (do_t . v_t) k_t,
+    dk_t = (do_t . v_t) q_t (+ dSn v_t at the last token), dv_t = (q_t . k_t) do_t (+ dSn^T k_t
+    at the last token), dS0 = 0 (n >= 1)."""
+    n, D = 6, 4
+    q, k, v, do = (rnd((n, 1, D), 60 + i) for i in range(4))
+    dSn = rnd((1, 1, D, D), 64)
+    S0 = rnd((1, 1, D, D), 65)
+    c = np.sum(do * v, axis=2, keepdims=True)
+    qk = np.sum(q * k, axis=2, keepdims=True)
+    wq, wk, wv = c * k, c * q, qk * do
+    wk[-1, 0] += dSn[0, 0] @ v[-1, 0]
+    wv[-1, 0] += dSn[0, 0].T @ k[-1, 0]
+    for fn in (o.backward, o.backward_recurrent):
+        dq, dk, dv, dS0 = fn(q, k, v, np.array([0.0]), do, init_state=S0, d_final=dSn)
+        close(dq, wq, 1e-14, "lambda=0 dq")
+        close(dk, wk, 1e-14, "lambda=0 dk")
+        close(dv, wv, 1e-14, "lambda=0 dv")
+        assert np.all(dS0 == 0.0), "lambda=0 dS0"
+
+
+def pin_backward_ones_closed_form(o):
+    """q = k = v = do = 1, no initial or final-state terms: dq_t = D (1 - lambda^(t+1)) / (1 - lambda),
+    dk_s = dv_s = D (1 - lambda^(n-s)) / (1 - lambda) (D (t+1), D (n-s) at lambda = 1), and
+    dS0 = sum_t lambda^(t+1) = lambda (1 - lambda^n) / (1 - lambda) (n at lambda = 1)."""
+    n, D = 29, 4
+    lams = np.array([0.0, 0.5, 0.9, 1.0])
+    H = len(lams)
+    one = np.ones((n, H, D))
+    t = np.arange(n, dtype=np.float64)
+    wq, wkv = np.zeros((n, H, D)), np.zeros((n, H, D))
+    wS = np.zeros((1, H, D, D))
+    for h, lam in enumerate(lams):
+        if lam == 1.0:
+            wq[:, h], wkv[:, h], wS[0, h] = (D * (t + 1))[:, None], (D * (n - t))[:, None], n
+        else:
+            wq[:, h] = (D * (1 - lam ** (t + 1)) / (1 - lam))[:, None]
+            wkv[:, h] = (D * (1 - lam ** (n - t)) / (1 - lam))[:, None]
+            wS[0, h] = lam * (1 - lam ** n) / (1 - lam)
+    for fn in (o.backward, o.backward_recurrent):
+        dq, dk, dv, dS0 = fn(one, one, one, lams, one)
+        close(dq, wq, 1e-13, "ones dq")
+        close(dk, wkv, 1e-13, "ones dk")
+        close(dv, wkv, 1e-13, "ones dv")
+        close(dS0, wS, 1e-13, "ones dS0")
+
+
+def pin_backward_homogeneity(o):
+    """o is linear in q, so <q, dq> = <do, o>; every term of L that holds k also holds v, so
+    <k, dk> = <v, dv>; L is affine in S0, so <S0, dS0> = L(S0) - L(0)."""
+    q, k, v, lams, cu, S0, do, dSn = _bwd_case(70)
+    dq, dk, dv, dS0 = o.backward(q, k, v, lams, do, cu, init_state=S0, d_final=dSn)
+    out = o.quadratic(q, k, v, lams, cu, init_state=S0)
+    close(np.sum(q * dq), np.sum(do * out), 1e-12, "<q,dq> = <do,o>")
+    close(np.sum(k * dk), np.sum(v * dv), 1e-12, "<k,dk> = <v,dv>")
+    l1 = _loss(o, q, k, v, lams, cu, S0, do, dSn)
+    l0 = _loss(o, q, k, v, lams, cu, np.zeros_like(S0), do, dSn)
+    close(np.sum(S0 * dS0), l1 - l0, 1e-12, "<S0,dS0> = L(S0) - L(0)")
+
+
+def pin_backward_varlen_is_concatenation(o):
+    """Packed gradients equal per-sequence gradients; an empty sequence gives dS0 = dSn."""
+    q, k, v, lams, cu, S0, do, dSn = _bwd_case(80)
+    for fn in (o.backward, o.backward_recurrent):
+        dq, dk, dv, dS0 = fn(q, k, v, lams, do, cu, init_state=S0, d_final=dSn)
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            if a == b:
+                close(dS0[s], dSn[s], 0.0, "empty sequence dS0")
+                continue
+            g = fn(q[a:b], k[a:b], v[a:b], lams, do[a:b], init_state=S0[s:s + 1],
+                   d_final=dSn[s:s + 1])
+            for name, x, y in zip(("dq", "dk", "dv"), (dq, dk, dv), g):
+                close(x[a:b], y, 1e-14, "varlen %s seq %d" % (name, s))
+            close(dS0[s], g[3][0], 1e-14, "varlen dS0 seq %d" % s)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_decode_worked_example,
@@ -326,4 +479,10 @@ ALL_PINS = [
     pin_initial_state_is_chunking,
     pin_decode_extends_prefill,
     pin_block_form,
+    pin_backward_finite_difference,
+    pin_backward_autograd,
+    pin_backward_lambda_zero,
+    pin_backward_ones_closed_form,
+    pin_backward_homogeneity,
+    pin_backward_varlen_is_concatenation,
 ]

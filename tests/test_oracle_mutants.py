@@ -50,6 +50,33 @@ MUTANTS = [
      "A[(size_t)s * n + t] = dot(q + (size_t)t * D, k + (size_t)s * D, D);", 0),
     ("varlen_rows_wrong_sequence_start", "if (t >= beg && t < end) break;",
      "if (t >= beg && t < end) { beg = 0; break; }", 0),
+    # backward, term-by-term form
+    ("bwd_dq_initial_state_undecayed", "g[a] += w * acc;", "g[a] += acc;", 0),
+    ("bwd_dq_initial_state_transposed", "acc += S0[(size_t)a * D + b] * dout_t[b];",
+     "acc += S0[(size_t)b * D + a] * dout_t[b];", 0),
+    ("bwd_dq_drops_diagonal", "for (int64_t s = t; s >= beg; --s) {\n            const double c",
+     "for (int64_t s = t - 1; s >= beg; --s) {\n            const double c", 0),
+    ("bwd_dk_drops_diagonal", "for (int64_t tp = t; tp < end; ++tp)",
+     "for (int64_t tp = t + 1; tp < end; ++tp)", 0),
+    ("bwd_dv_uses_dk_coefficient", "gv[a] += cv * dp[a];", "gv[a] += ck * dp[a];", 0),
+    ("bwd_dv_final_grad_not_transposed", "accv += dSn[(size_t)b * D + a] * kt[b];",
+     "accv += dSn[(size_t)a * D + b] * kt[b];", 0),
+    ("bwd_dk_final_grad_exponent", "for (int64_t m = t; m < end - 1; ++m) wn *= lam;",
+     "for (int64_t m = t; m < end; ++m) wn *= lam;", 0),
+    ("bwd_dinit_exponent_off_by_one", "double w = lam; /* lambda^(t+1) at t = beg */",
+     "double w = 1.0; /* lambda^(t+1) at t = beg */", 0),
+    ("bwd_dinit_final_grad_undecayed", "g[e] += wn * dSn[e];", "g[e] += dSn[e];", 0),
+    # backward, scan form
+    ("bwdrec_dq_state_transposed", "acc += St[(size_t)a * D + b] * dt[b];",
+     "acc += St[(size_t)b * D + a] * dt[b];", 0),
+    ("bwdrec_decays_before_last_token", "const double w = t == end - 1 ? 1.0 : lam;",
+     "const double w = lam;", 0),
+    ("bwdrec_dv_not_transposed", "accv += G[(size_t)b * D + a] * kt[b];",
+     "accv += G[(size_t)a * D + b] * kt[b];", 0),
+    ("bwdrec_dk_from_k", "acck += G[(size_t)a * D + b] * vt[b];",
+     "acck += G[(size_t)a * D + b] * kt[b];", 0),
+    ("bwdrec_dinit_missing_lambda", "const double w = end > beg ? lam : 1.0;",
+     "const double w = 1.0;", 0),
 ]
 
 

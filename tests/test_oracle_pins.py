@@ -37,3 +37,20 @@ def test_oracle_regression_fixture(orc):
     st = orc.final_state(k, v, lam, cu, init_state=S0)
     assert np.allclose(out, np.array(doc["out"]), rtol=1e-13, atol=1e-13)
     assert np.allclose(st, np.array(doc["final_state"]), rtol=1e-13, atol=1e-13)
+
+
+def test_oracle_backward_regression_fixture(orc):
+    """The backward oracle still reproduces the gradients stored in the same fixture."""
+    import json
+    import os
+
+    import numpy as np
+
+    from golden.make_golden import backward_case
+
+    doc = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                      "oracle_regression.json")))
+    q, k, v, lam, cu, S0, d_out, d_final = backward_case()
+    got = orc.backward(q, k, v, lam, d_out, cu, init_state=S0, d_final=d_final)
+    for name, g in zip(("dq", "dk", "dv", "d_init"), got):
+        assert np.allclose(g, np.array(doc[name]), rtol=1e-13, atol=1e-13), name
