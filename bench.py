@@ -166,6 +166,7 @@ def main():
     if not args.no_extras:
         del q, k, v, out
         result["few_chain_prefill"] = few_chain_prefill(dev)
+        result["backward"] = backward_leg(wl, dev)
     if not args.no_cpu_baseline:
         q, k, v = wl.inputs(device=dev)
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)
@@ -187,6 +188,33 @@ def time_ms(fn, iters, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters
+
+
+def backward_bytes(T, H, D, S=1):
+    # read q, k, v, d_out and write dq, dk, dv (bf16) + write d_initial_state (fp32)
+    return T * H * D * 2 * 7 + S * H * D * D * 4 + H * 4
+
+
+def backward_leg(wl, dev, iters=10, warmup=2):
+    """Backward of the 65,536 x 64 prefill (dq, dk, dv and the initial-state gradient), timed
+    outside the timed steps."""
+    import torch
+
+    import long_context_attention_attn_amd as la
+    from long_context_attention_attn_amd import synth
+
+    q, k, v = wl.inputs(device=dev)
+    do, _, _ = synth.qkv(wl.T, wl.H, wl.D, torch.bfloat16, seed=50, device=dev)
+    dec = wl.decay().to(dev)
+    ms = time_ms(lambda: la.backward(q, k, v, dec, do), iters, warmup)
+    nbytes = backward_bytes(wl.T, wl.H, wl.D)
+    # three scans: each reads three [T, H, D] tensors and writes one
+    scan_bytes = 3 * prefill_bytes(wl.T, wl.H, wl.D)
+    return {"tokens": wl.T, "heads": wl.H, "ms": ms, "tokens_per_s": wl.T / (ms / 1e3),
+            "algorithmic_bytes": nbytes, "algorithmic_GBps": nbytes / (ms / 1e3) / 1e9,
+            "scan_bytes": scan_bytes, "scan_GBps": scan_bytes / (ms / 1e3) / 1e9,
+            "flop": 3 * prefill_flop(wl.T, wl.H, wl.D),
+            "tflops": 3 * prefill_flop(wl.T, wl.H, wl.D) / (ms / 1e3) / 1e12}
 
 
 def few_chain_prefill(dev, iters=20, warmup=3):

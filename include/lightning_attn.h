@@ -1,5 +1,6 @@
 /*
- * lightning_attn.h -- C ABI of the MI355X (gfx950) lightning-attention forward library.
+ * lightning_attn.h -- C ABI of the MI355X (gfx950) lightning-attention library: prefill,
+ * sequence-split prefill, backward and decode.
  *
  * The operation.  Lightning attention is causal linear attention computed block by block:
  * inside a block the left product ((Q K^T) masked) V, across blocks the right product
@@ -129,6 +130,38 @@ size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t 
  * at least 4 blocks per segment; 0 when splitting would not add parallelism (the plain launch
  * already has a workgroup per compute unit, or no sequence would be cut) or on any error. */
 int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D);
+
+/*
+ * Backward of la_prefill_ex: gradients of a loss L given dL/dout (d_out) and, optionally,
+ * dL/dfinal_state (d_final_state).  The pages give no backward pass (they state training at up
+ * to 1M tokens of context: abstract of the MiniMax-01 report; digest, section 2); these are the
+ * derivatives of the operation defined at the top of this header, per sequence and head with
+ * local token indices and n tokens:
+ *
+ *   dq_t = sum_{s<=t} lambda^(t-s) (do_t . v_s) k_s  + lambda^(t+1) S0 do_t
+ *   dk_s = sum_{t>=s} lambda^(t-s) (do_t . v_s) q_t  + lambda^(n-1-s) dSn v_s
+ *   dv_s = sum_{t>=s} lambda^(t-s) (q_t . k_s) do_t  + lambda^(n-1-s) dSn^T k_s
+ *   dS0  = sum_t lambda^(t+1) q_t^T do_t + lambda^n dSn
+ *
+ * Each is a scan of the same block form as the prefill: dq is the forward scan with
+ * (query, key, value) = (do, v, k) from S0^T; dk and dv are reversed-time scans with (v, do, q)
+ * from dSn^T and (k, q, do) from dSn; dS0 is lambda times the last of these scans' final
+ * state.  Three launches on `stream`, no workspace.  lambda gets no gradient (a constant).
+ *
+ *   q, k, v, decay, cu_seqlens, initial_state: the forward call's inputs (initial_state may be
+ *                 NULL = zeros)
+ *   d_out         in  [T][H][D] dtype
+ *   d_final_state in  [S][H][D][D] float32, or NULL (= zeros)
+ *   dq, dk, dv    out [T][H][D] dtype, distinct, not aliasing any input
+ *   d_initial_state out [S][H][D][D] float32, or NULL to skip
+ * Errors: as la_prefill_ex, plus LA_ERR_INVALID_ARG for a NULL, misaligned or aliasing gradient
+ * buffer.
+ */
+la_status la_backward(const void *q, const void *k, const void *v, const float *decay,
+                      const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
+                      const float *d_final_state, void *dq, void *dk, void *dv,
+                      float *d_initial_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                      la_dtype dtype, void *stream);
 
 /*
  * One recurrent decode step for Bt independent sequences (one new token each):

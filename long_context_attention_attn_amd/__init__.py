@@ -21,7 +21,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["prefill", "decode_step", "LightningAttnError", "library_path"]
+__all__ = ["prefill", "backward", "lightning_attention", "decode_step", "LightningAttnError",
+           "library_path"]
 
 LightningAttnError = _lib.LightningAttnError
 library_path = _lib.library_path
@@ -122,6 +123,81 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
     else:
         _lib.prefill_ex(*ptrs, T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
     return out, final_state
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,
+             d_out: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None, *,
+             initial_state: Optional[torch.Tensor] = None,
+             d_final_state: Optional[torch.Tensor] = None,
+             want_d_initial_state: bool = True):
+    """Gradients of the prefill: (dq, dk, dv [T, H, D], d_initial_state [S, H, D, D] or None).
+
+    q, k, v, decay, cu_seqlens, initial_state: the prefill's inputs; d_out [T, H, D] (same dtype
+    as q) is dL/dout, d_final_state [S, H, D, D] fp32 (or None = 0) is dL/dfinal_state."""
+    device = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, D]")
+    T, H, D = q.shape
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    for name, x in (("q", q), ("k", k), ("v", v), ("d_out", d_out)):
+        _check_act(name, x, dtype, device)
+        if x.shape != q.shape:
+            raise ValueError("%s must be [T, H, D]" % name)
+    _check_act("decay", decay, torch.float32, device)
+    if decay.shape != (H,):
+        raise ValueError("decay must be [H]")
+    if cu_seqlens is not None:
+        _check_act("cu_seqlens", cu_seqlens, torch.int32, device)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [S+1] with S >= 1")
+        S = cu_seqlens.numel() - 1
+    else:
+        S = 1
+    for name, x in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if x is not None:
+            _check_act(name, x, torch.float32, device)
+            if x.shape != (S, H, D, D):
+                raise ValueError("%s must be [S, H, D, D]" % name)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    d_init = (torch.empty((S, H, D, D), dtype=torch.float32, device=device)
+              if want_d_initial_state else None)
+    _lib.backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
+                  0 if cu_seqlens is None else cu_seqlens.data_ptr(),
+                  0 if initial_state is None else initial_state.data_ptr(), d_out.data_ptr(),
+                  0 if d_final_state is None else d_final_state.data_ptr(), dq.data_ptr(),
+                  dk.data_ptr(), dv.data_ptr(), 0 if d_init is None else d_init.data_ptr(),
+                  T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
+    return dq, dk, dv, d_init
+
+
+class _LightningAttention(torch.autograd.Function):
+    """prefill as a differentiable op (gradients for q, k, v and the initial state)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, decay, cu_seqlens, initial_state, split):
+        out, fs = prefill(q, k, v, decay, cu_seqlens, initial_state=initial_state, split=split)
+        ctx.save_for_backward(q, k, v, decay, cu_seqlens, initial_state)
+        return out, fs
+
+    @staticmethod
+    def backward(ctx, d_out, d_fs):
+        q, k, v, decay, cu_seqlens, initial_state = ctx.saved_tensors
+        dq, dk, dv, d_init = backward(
+            q, k, v, decay, d_out.contiguous(), cu_seqlens, initial_state=initial_state,
+            d_final_state=None if d_fs is None else d_fs.contiguous(),
+            want_d_initial_state=initial_state is not None and ctx.needs_input_grad[5])
+        return dq, dk, dv, None, None, d_init, None
+
+
+def lightning_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,
+                        cu_seqlens: Optional[torch.Tensor] = None,
+                        initial_state: Optional[torch.Tensor] = None,
+                        split: Union[None, str, int] = None):
+    """Differentiable prefill: (out, final_state); backward runs the library's gradient
+    scans.  decay and cu_seqlens get no gradient."""
+    return _LightningAttention.apply(q, k, v, decay, cu_seqlens, initial_state, split)
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,

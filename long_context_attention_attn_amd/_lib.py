@@ -21,7 +21,8 @@ LA_F32, LA_BF16 = 0, 1
 
 # Every symbol declared in include/lightning_attn.h.
 EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_split",
-           "la_prefill_split_workspace_size", "la_prefill_split_blocks", "la_decode_step",
+           "la_prefill_split_workspace_size", "la_prefill_split_blocks", "la_backward",
+           "la_decode_step",
            "la_status_str", "la_last_error")
 
 _lock = threading.Lock()
@@ -71,6 +72,9 @@ def load():
         lib.la_prefill_split_workspace_size.restype = ctypes.c_size_t
         lib.la_prefill_split_blocks.argtypes = [i64, i32, i32, i32]
         lib.la_prefill_split_blocks.restype = i32
+        lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32,
+                                    i32, i32, ctypes.c_int, vp]
+        lib.la_backward.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_status_str.argtypes = [ctypes.c_int]
@@ -115,6 +119,13 @@ def prefill_split_workspace_size(T, S, H, D, seg_blocks) -> int:
 
 def prefill_split_blocks(T, S, H, D) -> int:
     return int(load().la_prefill_split_blocks(T, S, H, D))
+
+
+def backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state, dq, dk, dv,
+             d_initial_state, T, S, H, D, dtype, stream):
+    _raise(load().la_backward(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens), _p(initial_state),
+                              _p(d_out), _p(d_final_state), _p(dq), _p(dk), _p(dv),
+                              _p(d_initial_state), T, S, H, D, dtype, _p(stream)))
 
 
 def decode_step(q, k, v, decay, state, out, Bt, H, D, dtype, stream):

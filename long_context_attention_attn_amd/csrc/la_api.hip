@@ -241,6 +241,88 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   return LA_OK;
 }
 
+la_status la_backward(const void *q, const void *k, const void *v, const float *decay,
+                      const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
+                      const float *d_final_state, void *dq, void *dk, void *dv,
+                      float *d_initial_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                      la_dtype dtype, void *stream) {
+  g_err[0] = '\0';
+  la_status st = check_common(q, k, v, decay, d_out, T, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (T > 0) {
+    if (!dq || !dk || !dv) return fail(LA_ERR_INVALID_ARG, "dq, dk or dv is NULL");
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+      return fail(LA_ERR_INVALID_ARG, "dq, dk and dv must be 16-byte aligned");
+    const void *in[4] = {q, k, v, d_out};
+    const void *grad[3] = {dq, dk, dv};
+    for (const void *g : grad) {
+      for (const void *x : in)
+        if (g == x) return fail(LA_ERR_INVALID_ARG, "a gradient output aliases an input");
+    }
+    if (dq == dk || dq == dv || dk == dv)
+      return fail(LA_ERR_INVALID_ARG, "dq, dk and dv must be distinct");
+  }
+  if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
+  if (cu_seqlens == nullptr && S != 1)
+    return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
+  if ((long long)S * H * (D / 32) > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "S*H too large");
+  if (d_initial_state != nullptr &&
+      (d_initial_state == initial_state || d_initial_state == d_final_state))
+    return fail(LA_ERR_INVALID_ARG, "d_initial_state aliases a state input");
+  if (T == 0 && d_initial_state == nullptr) return LA_OK;
+  st = check_device();
+  if (st != LA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto scan = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
+
+  LaPrefillArgs a{};
+  a.decay = decay;
+  a.cu_seqlens = cu_seqlens;
+  a.T = T;
+  a.S = S;
+  a.H = H;
+  a.D = D;
+  hipError_t e;
+  if (T > 0) {
+    // dq_t = sum_{s<=t} lambda^(t-s) (do_t . v_s) k_s + lambda^(t+1) S0 do_t: the forward scan
+    // with (query, key, value) = (do, v, k) and the initial state transposed.
+    a.q = d_out;
+    a.k = v;
+    a.v = k;
+    a.initial_state = initial_state;
+    a.init_transposed = true;
+    a.out = dq;
+    e = scan(a, s);
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "dq launch: %s", hipGetErrorString(e));
+    // dk_s = sum_{t>=s} lambda^(t-s) (v_s . do_t) q_t + lambda^(n-1-s) dSn v_s: the reversed
+    // scan with (v, do, q), dSn transposed as an initial state weighted lambda^t.
+    a.q = v;
+    a.k = d_out;
+    a.v = q;
+    a.initial_state = d_final_state;
+    a.reverse = true;
+    a.init_inclusive = true;
+    a.out = dk;
+    e = scan(a, s);
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "dk launch: %s", hipGetErrorString(e));
+  }
+  // dv_s = sum_{t>=s} lambda^(t-s) (k_s . q_t) do_t + lambda^(n-1-s) dSn^T k_s: the reversed
+  // scan with (k, q, do) and dSn as is; its final state times lambda is
+  // dS0 = sum_t lambda^(t+1) q_t^T do_t + lambda^n dSn (dSn itself for an empty sequence).
+  a.q = k;
+  a.k = q;
+  a.v = d_out;
+  a.initial_state = d_final_state;
+  a.reverse = true;
+  a.init_inclusive = true;
+  a.init_transposed = false;
+  a.out = dv;
+  a.final_state = d_initial_state;
+  e = scan(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dv launch: %s", hipGetErrorString(e));
+  return LA_OK;
+}
+
 la_status la_decode_step(const void *q, const void *k, const void *v, const float *decay,
                          float *state, void *out, int32_t Bt, int32_t H, int32_t D,
                          la_dtype dtype, void *stream) {

@@ -480,6 +480,9 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   // Block 0 decays the initial state by lambda^(b0 - 1) when it counts as inclusive.
   const int b0 = c.nb == 1 ? b_last : BLK;
   const float lb_first = c.incl ? pw[b0 - 1] : pw[b0];
+  // Scale of the final state: lambda for an inclusive initial state (read now: the powers
+  // table is overwritten by the pipeline's DMAs).
+  const float fsc = c.incl && c.nb > 0 ? pw[1] : 1.f;
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
 
   auto issue = [&](int blk) {
@@ -535,7 +538,6 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (fs) {
-    const float fsc = c.incl && c.nb > 0 ? pw[1] : 1.f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll

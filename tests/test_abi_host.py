@@ -148,3 +148,35 @@ def test_split_without_device(lib):
         pytest.skip("a GPU is visible")
     assert lib.la_prefill_split_blocks(8192, 1, 8, 128) == 0
     assert _split(lib) == 3
+
+
+G1, G2, G3 = ctypes.c_void_p(0x400000), ctypes.c_void_p(0x500000), ctypes.c_void_p(0x600000)
+
+
+def _backward(lib, dq=G1, dk=G2, dv=G3, d_out=P2, dinit=None, init=None, dfs=None, T=64, S=1,
+              D=128, q=P):
+    return lib.la_backward(q, P, P, P, None, init, d_out, dfs, dq, dk, dv, dinit, T, S, 2, D, 1,
+                           None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dq=None), 1), (dict(dv=None), 1), (dict(d_out=None), 1),
+    (dict(dk=ctypes.c_void_p(0x500004)), 1), (dict(dq=P), 1), (dict(dk=P2), 1),
+    (dict(dv=G1), 1), (dict(dinit=P2, init=P2), 1), (dict(dinit=G1, dfs=G1), 1),
+    (dict(S=0), 1), (dict(D=80), 2),
+])
+def test_backward_validation(lib, kwargs, status):
+    assert _backward(lib, **kwargs) == status
+    assert lib.la_last_error() != b""
+
+
+def test_backward_empty_without_state_grad_is_noop(lib):
+    assert _backward(lib, q=None, d_out=None, dq=None, dk=None, dv=None, T=0) == 0
+
+
+def test_backward_without_device(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _backward(lib) == 3
