@@ -167,6 +167,7 @@ def main():
         del q, k, v, out
         result["few_chain_prefill"] = few_chain_prefill(dev)
         result["backward"] = backward_leg(wl, dev)
+        result["decode_tokens"] = decode_tokens_leg(dev)
     if not args.no_cpu_baseline:
         q, k, v = wl.inputs(device=dev)
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)
@@ -215,6 +216,32 @@ def backward_leg(wl, dev, iters=10, warmup=2):
             "scan_bytes": scan_bytes, "scan_GBps": scan_bytes / (ms / 1e3) / 1e9,
             "flop": 3 * prefill_flop(wl.T, wl.H, wl.D),
             "tflops": 3 * prefill_flop(wl.T, wl.H, wl.D) / (ms / 1e3) / 1e12}
+
+
+def decode_tokens_leg(dev, iters=20, warmup=3):
+    """m decode steps per sequence in one pass (state read and written once) for 256 sequences
+    x 64 heads; m = 1 is the single-step kernel."""
+    import torch
+
+    import long_context_attention_attn_amd as la
+    from long_context_attention_attn_amd import synth
+
+    dec = synth.decay_geometric(H, 0.9, 0.9999).to(dev)
+    st = synth.random_state(BT_DECODE, H, D, seed=1, device=dev, scale=0.1)
+    res = []
+    for m in (1, 2, 4, 8):
+        q, k, v = synth.qkv(BT_DECODE * m, H, D, torch.bfloat16, seed=2, device=dev)
+        if m == 1:
+            fn = lambda: la.decode_step(q, k, v, dec, st)
+        else:
+            shp = (BT_DECODE, m, H, D)
+            q4, k4, v4 = q.view(shp), k.view(shp), v.view(shp)
+            fn = lambda: la.decode_tokens(q4, k4, v4, dec, st)
+        ms = time_ms(fn, iters, warmup)
+        nbytes = 2 * BT_DECODE * H * D * D * 4 + 4 * BT_DECODE * m * H * D * 2 + H * 4
+        res.append({"m": m, "ms": ms, "tokens_per_s": BT_DECODE * m / (ms / 1e3),
+                    "GBps": nbytes / (ms / 1e3) / 1e9, "bytes": nbytes})
+    return res
 
 
 def few_chain_prefill(dev, iters=20, warmup=3):

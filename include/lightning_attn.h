@@ -173,6 +173,20 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const floa
                          float *state, void *out, int32_t Bt, int32_t H, int32_t D,
                          la_dtype dtype, void *stream);
 
+/*
+ * m decode steps per sequence in one pass (speculative or chunked decode): for i = 0..m-1,
+ *   S <- lambda S + k_i^T v_i ;  o_i = q_i S
+ * with the state read and written once for all m tokens, so the step's HBM traffic per token
+ * falls as 1/m.  Same result as m calls of la_decode_step (and as la_prefill_ex over sequences
+ * of m tokens from the states), up to rounding order.
+ *   q, k, v in [Bt][m][H][D] dtype (token i of sequence b is row b*m + i of a [Bt*m][H][D]
+ *   packed tensor); out [Bt][m][H][D] dtype; state in/out [Bt][H][D][D] float32; m >= 1.
+ * Errors as la_decode_step, plus LA_ERR_INVALID_ARG for m < 1.
+ */
+la_status la_decode_tokens(const void *q, const void *k, const void *v, const float *decay,
+                           float *state, void *out, int32_t Bt, int32_t m, int32_t H, int32_t D,
+                           la_dtype dtype, void *stream);
+
 /* Static string naming a status code. */
 const char *la_status_str(la_status s);
 

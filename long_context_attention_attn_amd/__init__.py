@@ -21,8 +21,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["prefill", "backward", "lightning_attention", "decode_step", "LightningAttnError",
-           "library_path"]
+__all__ = ["prefill", "backward", "lightning_attention", "decode_step", "decode_tokens",
+           "LightningAttnError", "library_path"]
 
 LightningAttnError = _lib.LightningAttnError
 library_path = _lib.library_path
@@ -230,4 +230,39 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.
             raise ValueError("out must be [Bt, H, D]")
     _lib.decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(), state.data_ptr(),
                      out.data_ptr(), Bt, H, D, _DTYPES[dtype], _stream_ptr(device))
+    return out
+
+
+def decode_tokens(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,
+                  state: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """m decode steps per sequence in one pass; ``state`` [Bt, H, D, D] fp32 is updated in place.
+
+    q, k, v: [Bt, m, H, D] bf16 or fp32 (token i of sequence b at [b, i]); decay [H] fp32.
+    Returns out [Bt, m, H, D]."""
+    device = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [Bt, m, H, D]")
+    Bt, m, H, D = q.shape
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_act(name, x, dtype, device)
+        if x.shape != q.shape:
+            raise ValueError("%s must be [Bt, m, H, D]" % name)
+    _check_act("decay", decay, torch.float32, device)
+    if decay.shape != (H,):
+        raise ValueError("decay must be [H]")
+    _check_act("state", state, torch.float32, device)
+    if state.shape != (Bt, H, D, D):
+        raise ValueError("state must be [Bt, H, D, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_act("out", out, dtype, device)
+        if out.shape != q.shape:
+            raise ValueError("out must be [Bt, m, H, D]")
+    _lib.decode_tokens(q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
+                       state.data_ptr(), out.data_ptr(), Bt, m, H, D, _DTYPES[dtype],
+                       _stream_ptr(device))
     return out

@@ -22,7 +22,7 @@ LA_F32, LA_BF16 = 0, 1
 # Every symbol declared in include/lightning_attn.h.
 EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_split",
            "la_prefill_split_workspace_size", "la_prefill_split_blocks", "la_backward",
-           "la_decode_step",
+           "la_decode_step", "la_decode_tokens",
            "la_status_str", "la_last_error")
 
 _lock = threading.Lock()
@@ -77,6 +77,9 @@ def load():
         lib.la_backward.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
         lib.la_decode_step.restype = ctypes.c_int
+        lib.la_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                         vp]
+        lib.la_decode_tokens.restype = ctypes.c_int
         lib.la_status_str.argtypes = [ctypes.c_int]
         lib.la_status_str.restype = ctypes.c_char_p
         lib.la_last_error.argtypes = []
@@ -131,6 +134,11 @@ def backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state, dq
 def decode_step(q, k, v, decay, state, out, Bt, H, D, dtype, stream):
     _raise(load().la_decode_step(_p(q), _p(k), _p(v), _p(decay), _p(state), _p(out), Bt, H, D,
                                  dtype, _p(stream)))
+
+
+def decode_tokens(q, k, v, decay, state, out, Bt, m, H, D, dtype, stream):
+    _raise(load().la_decode_tokens(_p(q), _p(k), _p(v), _p(decay), _p(state), _p(out), Bt, m, H,
+                                   D, dtype, _p(stream)))
 
 
 def raw_status(fn: str, *args) -> int:

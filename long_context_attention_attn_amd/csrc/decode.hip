@@ -85,6 +85,80 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(const T *__restrict__ q,
   }
 }
 
+// Several tokens per sequence in one pass (speculative or chunked decode): the state block of
+// this thread (ROWS rows x 4 columns) stays in registers while the m tokens are applied in
+// order, S <- lambda S + k_i^T v_i, o_i = q_i S; the tokens are staged through LDS in chunks of
+// MT, and each chunk's m partial outputs are reduced through LDS.  The state is read and written
+// once for all m tokens.  Token i of sequence b is row b*m + i of the [Bt*m][H][D] activations.
+template <int D, typename T, int MT>
+__global__ __launch_bounds__(NTHR) void decode_multi_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ decay, float *__restrict__ state, T *__restrict__ out, int H,
+    int m) {
+  constexpr int QUADS = D / 4;
+  constexpr int RG = NTHR / QUADS;
+  constexpr int ROWS = D / RG;
+  __shared__ float qs[MT][D], ks[MT][D], vs[MT][D];
+  __shared__ float red[MT][RG][D + 4];
+
+  const int bh = blockIdx.x;  // = b * H + h
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x;
+  const int cq = tid % QUADS, rg = tid / QUADS;
+  const float lam = decay[h];
+  f32x4 *S4 = (f32x4 *)(state + (size_t)bh * D * D);
+  f32x4 st[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) st[r] = __builtin_nontemporal_load(S4 + (rg + RG * r) * QUADS + cq);
+
+  for (int c0 = 0; c0 < m; c0 += MT) {
+    const int mt = m - c0 < MT ? m - c0 : MT;
+    for (int e = tid; e < MT * D; e += NTHR) {
+      const int i = e / D, d = e % D;
+      const int64_t off = (((int64_t)b * m + c0 + i) * H + h) * D + d;
+      const bool ok = i < mt;
+      qs[i][d] = ok ? ld<T>(q, off) : 0.f;
+      ks[i][d] = ok ? ld<T>(k, off) : 0.f;
+      vs[i][d] = ok ? ld<T>(v, off) : 0.f;
+    }
+    __syncthreads();
+    f32x4 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < mt) {
+        const f32x4 vv = {vs[i][4 * cq], vs[i][4 * cq + 1], vs[i][4 * cq + 2], vs[i][4 * cq + 3]};
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const int a = rg + RG * r;
+          const float ka = ks[i][a], qa = qs[i][a];
+          st[r].x = fmaf(lam, st[r].x, ka * vv.x);
+          st[r].y = fmaf(lam, st[r].y, ka * vv.y);
+          st[r].z = fmaf(lam, st[r].z, ka * vv.z);
+          st[r].w = fmaf(lam, st[r].w, ka * vv.w);
+          acc[i].x = fmaf(qa, st[r].x, acc[i].x);
+          acc[i].y = fmaf(qa, st[r].y, acc[i].y);
+          acc[i].z = fmaf(qa, st[r].z, acc[i].z);
+          acc[i].w = fmaf(qa, st[r].w, acc[i].w);
+        }
+      }
+      *(f32x4 *)&red[i][rg][4 * cq] = acc[i];
+    }
+    __syncthreads();
+    for (int e = tid; e < mt * D; e += NTHR) {
+      const int i = e / D, col = e % D;
+      float o = 0.f;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) o += red[i][r][col];
+      out[(((int64_t)b * m + c0 + i) * H + h) * D + col] = (T)o;
+    }
+    __syncthreads();  // LDS reused by the next chunk
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r)
+    __builtin_nontemporal_store(st[r], S4 + (rg + RG * r) * QUADS + cq);
+}
+
 template <typename T>
 hipError_t launch(const LaDecodeArgs &a, hipStream_t stream) {
   const long long grid = (long long)a.Bt * a.H;
@@ -100,6 +174,22 @@ hipError_t launch(const LaDecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_multi(const LaDecodeArgs &a, int32_t m, hipStream_t stream) {
+  constexpr int MT = 8;
+  const long long grid = (long long)a.Bt * a.H;
+  if (grid <= 0 || m <= 0) return hipSuccess;
+  if (a.D == 128)
+    hipLaunchKernelGGL((decode_multi_kernel<128, T, MT>), dim3((unsigned)grid), dim3(NTHR), 0,
+                       stream, (const T *)a.q, (const T *)a.k, (const T *)a.v, a.decay, a.state,
+                       (T *)a.out, a.H, m);
+  else
+    hipLaunchKernelGGL((decode_multi_kernel<64, T, MT>), dim3((unsigned)grid), dim3(NTHR), 0,
+                       stream, (const T *)a.q, (const T *)a.k, (const T *)a.v, a.decay, a.state,
+                       (T *)a.out, a.H, m);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t la_launch_decode_bf16(const LaDecodeArgs &a, hipStream_t stream) {
@@ -107,4 +197,10 @@ hipError_t la_launch_decode_bf16(const LaDecodeArgs &a, hipStream_t stream) {
 }
 hipError_t la_launch_decode_f32(const LaDecodeArgs &a, hipStream_t stream) {
   return launch<float>(a, stream);
+}
+hipError_t la_launch_decode_multi_bf16(const LaDecodeArgs &a, int32_t m, hipStream_t stream) {
+  return launch_multi<__bf16>(a, m, stream);
+}
+hipError_t la_launch_decode_multi_f32(const LaDecodeArgs &a, int32_t m, hipStream_t stream) {
+  return launch_multi<float>(a, m, stream);
 }

@@ -351,4 +351,35 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const floa
   return LA_OK;
 }
 
+la_status la_decode_tokens(const void *q, const void *k, const void *v, const float *decay,
+                           float *state, void *out, int32_t Bt, int32_t m, int32_t H, int32_t D,
+                           la_dtype dtype, void *stream) {
+  g_err[0] = '\0';
+  if (m < 1) return fail(LA_ERR_INVALID_ARG, "m = %d < 1 tokens per sequence", m);
+  if (Bt < 0) return fail(LA_ERR_INVALID_ARG, "negative batch %d", Bt);
+  la_status st = check_common(q, k, v, decay, out, (int64_t)Bt * m, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (Bt == 0) return LA_OK;
+  if (state == nullptr) return fail(LA_ERR_INVALID_ARG, "state is NULL");
+  if (!aligned16(state)) return fail(LA_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  if ((long long)Bt * H > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "Bt*H too large");
+  st = check_device();
+  if (st != LA_OK) return st;
+  LaDecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.state = state;
+  a.out = out;
+  a.Bt = Bt;
+  a.H = H;
+  a.D = D;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dtype == LA_BF16 ? la_launch_decode_multi_bf16(a, m, s)
+                                  : la_launch_decode_multi_f32(a, m, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return LA_OK;
+}
+
 }  // extern "C"

@@ -36,6 +36,9 @@ hipError_t la_launch_prefill_bf16(const LaPrefillArgs &a, hipStream_t stream);
 hipError_t la_launch_prefill_f32(const LaPrefillArgs &a, hipStream_t stream);
 hipError_t la_launch_decode_bf16(const LaDecodeArgs &a, hipStream_t stream);
 hipError_t la_launch_decode_f32(const LaDecodeArgs &a, hipStream_t stream);
+// m tokens per sequence (activations [Bt*m][H][D], token i of sequence b at row b*m + i).
+hipError_t la_launch_decode_multi_bf16(const LaDecodeArgs &a, int32_t m, hipStream_t stream);
+hipError_t la_launch_decode_multi_f32(const LaDecodeArgs &a, int32_t m, hipStream_t stream);
 
 // Sequence split (split.hip).
 hipError_t la_launch_seg_table(const int32_t *cu, int64_t T, int32_t S, int64_t seg_len,

@@ -180,3 +180,15 @@ def test_backward_without_device(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert _backward(lib) == 3
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(m=0), 1), (dict(m=-1), 1), (dict(Bt=-1), 1), (dict(state=None), 1),
+    (dict(state=MISALIGNED), 1), (dict(D=100), 2), (dict(q=None), 1),
+])
+def test_decode_tokens_validation(lib, kwargs, status):
+    a = dict(q=P, k=P, v=P, decay=P, state=P2, out=P, Bt=4, m=3, H=2, D=128, dt=1)
+    a.update(kwargs)
+    rc = lib.la_decode_tokens(a["q"], a["k"], a["v"], a["decay"], a["state"], a["out"], a["Bt"],
+                              a["m"], a["H"], a["D"], a["dt"], None)
+    assert rc == status
