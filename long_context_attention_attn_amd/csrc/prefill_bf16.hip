@@ -116,22 +116,91 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
                                            RSRC_WORD3);
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
-// lds_base + 16 l (lds_base wave-uniform).  Written as inline assembly so that the compiler
-// does not track it; completion is waited for explicitly (vmcnt) before the barrier that
-// publishes a stage.  Out-of-range offsets (buffer range check) read as zero.  M0 (the LDS
-// address) is saved and restored; the s_nop is the wait state an M0 write needs before an
-// LDS DMA reads it.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+// Direct global -> LDS copies of 16 bytes per lane: lane l's bytes land at LDS address m + 16 l
+// for the wave-uniform LDS address m of each copy.  Written as inline assembly so that the
+// compiler does not track them; completion is waited for explicitly (vmcnt) before the barrier
+// that publishes a stage.  Out-of-range offsets (buffer range check) read as zero.  M0 (the LDS
+// address) is saved once per batch of copies and restored after it; each s_nop is the wait
+// state an M0 write needs before an LDS DMA reads it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t o0, uint32_t m0) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_base), "v"(voff), "s"(r)
+      : "v"(o0), "s"(m0), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void dma16x2(__amdgpu_buffer_rsrc_t r, uint32_t o0, uint32_t o1,
+                                        uint32_t m0, uint32_t m1) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "s"(m0), "s"(m1), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void dma16x4(__amdgpu_buffer_rsrc_t r, uint32_t o0, uint32_t o1,
+                                        uint32_t o2, uint32_t o3, uint32_t m0, uint32_t m1,
+                                        uint32_t m2, uint32_t m3) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %4, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(m0), "s"(m1), "s"(m2), "s"(m3), "s"(r)
+      : "memory");
+}
+// One offset, one LDS address, two or three descriptors (the L2 prefetches of k, v [and q]).
+__device__ __forceinline__ void dma16_same2(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            uint32_t o, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %4, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o), "s"(m0), "s"(ra), "s"(rb)
+      : "memory");
+}
+__device__ __forceinline__ void dma16_same3(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            __amdgpu_buffer_rsrc_t rc, uint32_t o, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %4, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o), "s"(m0), "s"(ra), "s"(rb), "s"(rc)
       : "memory");
 }
 
@@ -162,94 +231,117 @@ __device__ __forceinline__ bf16x4 tr_read(const char *p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Byte offset of (row, element col) in a swizzled [rows][D] bf16 tile: 16-byte chunk c of row
-// r is stored at chunk position c ^ (r % CH), so 16 lanes reading one chunk column of 16
-// consecutive rows hit 16 different bank groups.
+// Swizzled tiles.  LDS has 64 banks of 4 bytes; the 16-byte chunks of a row are permuted so
+// that every access pattern of the kernel touches each bank once per cycle:
+//  * Q/K tiles and the bf16 state copy ([rows][D], chunk c of row r at position c ^ f(r)):
+//    16 lanes reading one chunk of 16 consecutive rows (16-byte reads), and 32 lanes reading two
+//    adjacent chunks of 8 consecutive rows (transpose reads of K).  f is a permutation of the 16
+//    row residues whose halves f(r) >> 1 differ within each group of 8 rows; at D = 64 (128-byte
+//    rows, two rows per bank line) the row's parity takes the role of the missing position bit.
+//  * V tiles and the decayed V copy ([64][32] bf16, 64-byte rows): chunk c of row r at position
+//    c ^ g(r), g(r) = 2 ((r >> 2) & 1), so the transpose reads of 8 rows x 2 chunks, whose rows
+//    r and r + 4 share a bank line, use its two halves.
+template <int D>
+__device__ __forceinline__ int swf(int row) {
+  return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : ((((row >> 1) & 3) << 1) | ((row >> 3) & 1));
+}
+// Byte offset of (row, element col) in a swizzled [rows][D] bf16 tile.
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
   using C = Cfg<D>;
-  return row * C::ROWB + ((((col >> 3) ^ row) & (C::CH - 1)) << 4) + ((col & 7) << 1);
+  return row * C::ROWB + ((((col >> 3) ^ swf<D>(row)) & (C::CH - 1)) << 4) + ((col & 7) << 1);
+}
+__device__ __forceinline__ int vswf(int row) { return ((row >> 2) & 1) << 1; }
+// Byte offset of (row, element col) in a swizzled [64][CV] bf16 V tile.
+__device__ __forceinline__ int vswz(int row, int col) {
+  return row * (2 * CV) + ((((col >> 3) ^ vswf(row)) & 3) << 4) + ((col & 7) << 1);
 }
 
 // Everything a wave needs about its workgroup's chain.
 struct Chain {
-  const __bf16 *q, *k, *v;
-  __bf16 *out;
-  int64_t tok0;  // first token of the sequence
-  int64_t n;     // its length
-  int nb;        // number of blocks
-  int H, h, c0;  // heads, this head, first value column of the slice
-  int slice;     // c0 / CV
-  bool rev;      // local token t is physical token n-1-t (anti-causal scan)
-  bool incl;     // initial state weighted lambda^t, final state times lambda
-  bool s0t;      // initial state read transposed
+  const char *q, *k, *v;  // byte address of (first token of the sequence, head h); v: full rows
+  char *out;              // byte address of (first token, head h, column c0) in out
+  int64_t n;              // sequence length
+  int nb;                 // number of blocks
+  int b_last;             // rows of the last block
+  uint32_t rowbytes;      // bytes per token row of q, k, v, out (H * D * 2)
+  int c0, slice;          // first value column of the slice, c0 / CV
+  bool incl;              // initial state weighted lambda^t, final state times lambda
+  bool s0t;               // initial state read transposed
 };
 
-// Where the rows of block `blk` lie: b rows exist (0 past the end); a buffer descriptor based
-// at element offset row0 and b rows long covers exactly them; local row r of the block is at
-// row first + dir * r of that range.  Forward: first = 0, dir = 1.  Reversed scan: the block's
-// local rows are the sequence's physical rows in descending order, first = b - 1, dir = -1, so
-// a local row past the end gets a negative row index, i.e. a byte offset of at least
-// 2^32 - 63 * rowbytes, which the range check rejects like any row past the end.
-struct BlockRows {
-  int b;
-  int64_t row0;
-  int first, dir;
+// Block blk of the chain: its b rows (0 past the end) lie in one contiguous byte range that
+// starts `off` bytes after the sequence's first row; a buffer descriptor over exactly that range
+// makes rows past the end read as zero and stores to them no-ops, with no branch.  A forward scan
+// maps local row r to range row r.  A reversed scan (local token t = physical token n-1-t) maps
+// it to range row b-1-r; for a local row past the end that row index is negative, i.e. a 32-bit
+// byte offset of at least 2^32 - 63 * rowbytes, which the range check rejects like any other.
+struct Span {
+  int64_t off;
+  uint32_t bytes;  // b * rowbytes
+  uint32_t last;   // (b - 1) * rowbytes
 };
-__device__ __forceinline__ BlockRows block_rows(const Chain &c, int blk) {
-  const int64_t rem = c.n - (int64_t)blk * BLK;
-  const int b = rem <= 0 ? 0 : (rem < BLK ? (int)rem : BLK);
-  int64_t t = c.tok0;  // lowest physical token of the block (the sequence start if b = 0)
-  if (b > 0) t += c.rev ? rem - b : (int64_t)blk * BLK;
-  return BlockRows{b, t * c.H + c.h, c.rev ? b - 1 : 0, c.rev ? -1 : 1};
+template <bool REV>
+__device__ __forceinline__ Span span(const Chain &c, int blk) {
+  const int b = blk < c.nb - 1 ? BLK : (blk == c.nb - 1 ? c.b_last : 0);
+  int64_t row = 0;
+  if (b > 0) row = REV ? c.n - (int64_t)blk * BLK - b : (int64_t)blk * BLK;
+  return Span{row * (int64_t)c.rowbytes, (uint32_t)b * c.rowbytes, (uint32_t)(b - 1) * c.rowbytes};
 }
-__device__ __forceinline__ uint32_t row_off(const BlockRows &br, int row, uint32_t rowbytes) {
-  return (uint32_t)((int64_t)(br.first + br.dir * row) * (int64_t)rowbytes);
+// Byte offset of byte `col` of local row `row` of a block, in two steps: lane_base once per wave
+// (row * rowbytes + col forward, row * rowbytes - col reversed), then at() per block.
+template <bool REV>
+__device__ __forceinline__ uint32_t lane_base(int row, uint32_t col, uint32_t rowbytes) {
+  return REV ? (uint32_t)row * rowbytes - col : (uint32_t)row * rowbytes + col;
+}
+template <bool REV>
+__device__ __forceinline__ uint32_t at(const Span &s, uint32_t base) {
+  return REV ? s.last - base : base;
 }
 
-// DMA 16 rows (16r..16r+15) of a [64][D] tile of block `blk` into its swizzled LDS image.
-template <int D>
-__device__ __forceinline__ void dma_rows(const __bf16 *base, const Chain &c, int blk, int r,
-                                         uint32_t lds_tile, int lane) {
+// Lane offsets of the DMA copies of rows 16r..16r+15 of a [64][D] tile (swizzled LDS image).
+template <int D, bool REV>
+__device__ __forceinline__ void rows_offsets(int r, int lane, uint32_t rowbytes, uint32_t *offs) {
   using C = Cfg<D>;
-  const BlockRows br = block_rows(c, blk);
-  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  const auto rs = rsrc(base + br.row0 * D, (uint32_t)br.b * rowbytes);
 #pragma unroll
   for (int a = 0; a < C::QK_DMA; ++a) {
     const int row = 16 * r + a * C::RPI + lane / C::CH;
-    const int chunk = (lane % C::CH) ^ (row % C::CH);
-    dma16(rs, row_off(br, row, rowbytes) + 16u * chunk,
-          lds_tile + (uint32_t)((16 * r + a * C::RPI) * C::ROWB));
+    const int chunk = (lane % C::CH) ^ swf<D>(row);  // lands at position lane % CH
+    offs[a] = lane_base<REV>(row, 16u * chunk, rowbytes);
   }
 }
-
-// DMA rows 16r..16r+15 of the V slice (32 columns, 64 bytes per row, unswizzled).
-template <int D>
-__device__ __forceinline__ void dma_vrows(const Chain &c, int blk, int r, uint32_t lds_tile,
-                                          int lane) {
+// DMA rows 16r..16r+15 of a [64][D] tile of the block at span s into LDS address lds (their
+// tile position), 1 KiB per copy.
+template <int D, bool REV>
+__device__ __forceinline__ void dma_rows(const char *base, const Span &s, const uint32_t *offs,
+                                         uint32_t lds) {
   using C = Cfg<D>;
-  const BlockRows br = block_rows(c, blk);
-  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  const auto rs = rsrc(c.v + br.row0 * D + c.c0, (uint32_t)br.b * rowbytes);
-  const int row = 16 * r + lane / 4;
-  dma16(rs, row_off(br, row, rowbytes) + 16u * (lane % 4), lds_tile + 16 * r * C::VROWB);
+  const auto rs = rsrc(base + s.off, s.bytes);
+  if constexpr (C::QK_DMA == 4)
+    dma16x4(rs, at<REV>(s, offs[0]), at<REV>(s, offs[1]), at<REV>(s, offs[2]), at<REV>(s, offs[3]),
+            lds, lds + 1024, lds + 2048, lds + 3072);
+  else
+    dma16x2(rs, at<REV>(s, offs[0]), at<REV>(s, offs[1]), lds, lds + 1024);
 }
 
-// Pull block `blk`'s rows 16s..16s+15 (s = this workgroup's value slice) of q, k and of the full
-// v rows into L2, several blocks before their DMA: one 16-byte read per 128-byte line, written to
-// a scratch area of LDS that nothing reads.  The D/32 slices of a head together cover all 64 rows
+// L2 prefetch of block rows 16s..16s+15 (s = this workgroup's value slice) of q, k and the full
+// v rows, several blocks before their DMA: one 16-byte read per 128-byte line, written to a
+// scratch area of LDS that nothing reads.  The D/32 slices of a head together cover all 64 rows
 // once, and the later DMAs of all four slices then hit L2 instead of waiting on HBM.
-template <int D, bool SO>
-__device__ __forceinline__ void prefetch_l2(const Chain &c, int blk, uint32_t sink, int lane) {
-  const BlockRows br = block_rows(c, blk);
-  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
-  const uint32_t bytes = (uint32_t)br.b * rowbytes;
-  const int row = 16 * c.slice + ((lane >> 1) & 15);
-  const uint32_t off = row_off(br, row, rowbytes) + (uint32_t)(lane & 1) * (D == 128 ? 128u : 64u);
-  if constexpr (!SO) dma16(rsrc(c.q + br.row0 * D, bytes), off, sink);
-  dma16(rsrc(c.k + br.row0 * D, bytes), off, sink);
-  dma16(rsrc(c.v + br.row0 * D, bytes), off, sink);
+template <int D, bool REV>
+__device__ __forceinline__ uint32_t prefetch_offset(int slice, int lane, uint32_t rowbytes) {
+  return lane_base<REV>(16 * slice + ((lane >> 1) & 15), (uint32_t)(lane & 1) * (D == 128 ? 128u : 64u),
+                        rowbytes);
+}
+template <bool SO, bool REV>
+__device__ __forceinline__ void prefetch_l2(const Chain &c, int blk, uint32_t off, uint32_t sink) {
+  const Span s = span<REV>(c, blk);
+  const uint32_t o = at<REV>(s, off);
+  if constexpr (SO)
+    dma16_same2(rsrc(c.k + s.off, s.bytes), rsrc(c.v + s.off, s.bytes), o, sink);
+  else
+    dma16_same3(rsrc(c.q + s.off, s.bytes), rsrc(c.k + s.off, s.bytes), rsrc(c.v + s.off, s.bytes),
+                o, sink);
 }
 // prefetch instructions per block (no Q when only the state is computed)
 template <bool SO>
@@ -264,7 +356,7 @@ constexpr int PF_AHEAD = 4; // blocks between a block's prefetch and its DMA
 // decayed, lambda^(b-1-j) V[j], to the double-buffered copy the state waves consume (so no state
 // wave scales operands).
 // ------------------------------------------------------------------------------------------
-template <int D, int R, bool SO>
+template <int D, int R, bool SO, bool REV>
 __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const float *pw,
                                             int lane) {
   using C = Cfg<D>;
@@ -298,10 +390,22 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
   // Block 0 applies the initial state; weighted lambda^j instead when it counts as inclusive.
   const float inter_first = c.incl ? pw[jrow] : inter_scale;
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
-  const uint32_t rowbytes = (uint32_t)c.H * D * 2;
+  const uint32_t rowbytes = c.rowbytes;
+  // Lane offsets of this wave's DMA copies (Q row groups R and, for wave 1, 3; V row groups) and
+  // of its output stores.
+  uint32_t qoff[2][C::QK_DMA];
+  rows_offsets<D, REV>(R, lane, rowbytes, qoff[0]);
+  rows_offsets<D, REV>(3, lane, rowbytes, qoff[1]);
+  uint32_t voff[NVG > 0 ? NVG : 1];
+#pragma unroll
+  for (int m = 0; m < NVG; ++m)
+    voff[m] = lane_base<REV>(16 * (VG0 + m) + lane / 4,
+                             16u * ((lane % 4) ^ vswf(16 * (VG0 + m) + lane / 4)), rowbytes);
+  const uint32_t ooff = lane_base<REV>(jrow, 8u * g, rowbytes);
+  const char *vslice = c.v + 2 * c.c0;
   // This wave's share of the decayed V copy: lane bytes 16 (lane % 4) .. +15 of V rows
   // 16 m + lane / 4, m in its groups, with their decay lambda^(b-1-row) (full and last block).
-  const int b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
+  const int b_last = c.b_last;
   float lv_full[NVG > 0 ? NVG : 1], lv_last[NVG > 0 ? NVG : 1];
 #pragma unroll
   for (int m = 0; m < NVG; ++m) {
@@ -312,10 +416,16 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 
   auto issue = [&](int blk) {
     const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
-    if constexpr (!SO && R < 3) dma_rows<D>(c.q, c, blk, R, st + C::Q_OFF, lane);
-    if constexpr (!SO && R == 1) dma_rows<D>(c.q, c, blk, 3, st + C::Q_OFF, lane);
-#pragma unroll
-    for (int m = 0; m < NVG; ++m) dma_vrows<D>(c, blk, VG0 + m, st + C::V_OFF, lane);
+    const Span sp = span<REV>(c, blk);
+    if constexpr (!SO && R < 3)
+      dma_rows<D, REV>(c.q, sp, qoff[0], st + C::Q_OFF + 16 * R * C::ROWB);
+    if constexpr (!SO && R == 1) dma_rows<D, REV>(c.q, sp, qoff[1], st + C::Q_OFF + 48 * C::ROWB);
+    const uint32_t vl = st + C::V_OFF + 16 * VG0 * C::VROWB;  // 1 KiB per 16-row group
+    if constexpr (NVG == 2)
+      dma16x2(rsrc(vslice + sp.off, sp.bytes), at<REV>(sp, voff[0]), at<REV>(sp, voff[1]), vl,
+              vl + 1024);
+    else if constexpr (NVG == 1)
+      dma16(rsrc(vslice + sp.off, sp.bytes), at<REV>(sp, voff[0]), vl);
   };
   // Decayed copy of this wave's V rows of block blk (landed) into buffer blk & 1.  All reads
   // are issued before any write, so the LDS round trips overlap.
@@ -380,8 +490,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const bf16x4 lo = tr_read(Vs + (32 * s + trow) * C::VROWB + 2 * (16 * ct + tcol));
-          const bf16x4 hi = tr_read(Vs + (32 * s + 16 + trow) * C::VROWB + 2 * (16 * ct + tcol));
+          const bf16x4 lo = tr_read(Vs + vswz(32 * s + trow, 16 * ct + tcol));
+          const bf16x4 hi = tr_read(Vs + vswz(32 * s + 16 + trow, 16 * ct + tcol));
           vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 
@@ -411,9 +521,9 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 
       // Store: lane holds O[jrow][c0 + 16ct + 4g + 0..3]; rows past the end are dropped.
       {
-        const BlockRows br = block_rows(c, i);
-        const auto ro = rsrc(c.out + br.row0 * D + c.c0, (uint32_t)br.b * rowbytes);
-        const uint32_t off = row_off(br, jrow, rowbytes) + 8u * g;
+        const Span sp = span<REV>(c, i);
+        const auto ro = rsrc(c.out + sp.off, sp.bytes);
+        const uint32_t off = at<REV>(sp, ooff);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(o[ct])), ro,
@@ -438,7 +548,7 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 // State wave r: its band of the fp32 state.  Issues the DMA of K rows 16r..16r+15; the lightest
 // state wave (r = 3) also issues the L2 prefetches.
 // ------------------------------------------------------------------------------------------
-template <int D, int R, bool SO>
+template <int D, int R, bool SO, bool REV>
 __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const float *pw,
                                            const float *s0, float *fs, size_t sbase, int lane) {
   using C = Cfg<D>;
@@ -475,7 +585,7 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   write_kvx(smem + C::KVX_OFF);
 
   // lambda^b for full blocks and for the last block, which may be partial (b_last rows).
-  const int b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
+  const int b_last = c.b_last;
   const float lb_full = pw[BLK], lb_last = pw[b_last];
   // Block 0 decays the initial state by lambda^(b0 - 1) when it counts as inclusive.
   const int b0 = c.nb == 1 ? b_last : BLK;
@@ -485,17 +595,20 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   const float fsc = c.incl && c.nb > 0 ? pw[1] : 1.f;
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
 
+  uint32_t koff[C::QK_DMA];
+  rows_offsets<D, REV>(R, lane, c.rowbytes, koff);
+  const uint32_t pfoff = prefetch_offset<D, REV>(c.slice, lane, c.rowbytes);
   auto issue = [&](int blk) {
     const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
-    dma_rows<D>(c.k, c, blk, R, st + C::K_OFF, lane);
+    dma_rows<D, REV>(c.k, span<REV>(c, blk), koff, st + C::K_OFF + 16 * R * C::ROWB);
     // after the DMA, so that waiting for this DMA never waits for a prefetch (counters are
     // in order)
-    if constexpr (PF) prefetch_l2<D, SO>(c, blk + PF_AHEAD, smem_lds + C::PF_OFF, lane);
+    if constexpr (PF) prefetch_l2<SO, REV>(c, blk + PF_AHEAD, pfoff, smem_lds + C::PF_OFF);
   };
   if constexpr (PF) {
     // Blocks NST-1 .. PF_AHEAD-1 are not covered by the prefetches of the first issues.
     for (int blk = NST - 1; blk < PF_AHEAD; ++blk)
-      prefetch_l2<D, SO>(c, blk, smem_lds + C::PF_OFF, lane);
+      prefetch_l2<SO, REV>(c, blk, pfoff, smem_lds + C::PF_OFF);
   }
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s);
@@ -516,8 +629,8 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
         bf16x8 vop[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const bf16x4 lo = tr_read(LVs + (32 * s + trow) * C::VROWB + 2 * (16 * ct + tcol));
-          const bf16x4 hi = tr_read(LVs + (32 * s + 16 + trow) * C::VROWB + 2 * (16 * ct + tcol));
+          const bf16x4 lo = tr_read(LVs + vswz(32 * s + trow, 16 * ct + tcol));
+          const bf16x4 hi = tr_read(LVs + vswz(32 * s + 16 + trow, 16 * ct + tcol));
           vop[ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
@@ -550,9 +663,9 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   }
 }
 
-// flags: bit 0 reversed scan, bit 1 inclusive initial state, bit 2 transposed initial state.
-// SO: compute only the final state (q and out are not touched).
-template <int D, bool SO>
+// flags: bit 1 inclusive initial state, bit 2 transposed initial state.  SO: compute only the
+// final state (q and out are not touched).  REV: reversed (anti-causal) scan.
+template <int D, bool SO, bool REV>
 __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
@@ -565,33 +678,43 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   // wave issues only after it has copied the powers it needs into registers.
   float *const pw = (float *)(smem + (NST - 1) * C::STAGE);
 
-  // Workgroup -> (chain = sequence*H + head, value slice); slices of a chain share an XCD.
+  // Workgroup -> (chain = sequence*H + head, value slice).  Workgroups are dealt to the 8 XCDs
+  // round-robin (wg % 8), so the slices of a chain share an XCD (and its L2, where the chain's
+  // Q and K lines are then fetched once) when chain c's slices are the workgroups
+  // 8 (NS (c / 8) + s) + c % 8.  That covers the largest multiple of 8 NS workgroups.  The
+  // R < 8 NS workgroups past it are numbered XCD by XCD (XCD x holds R / 8 of them, one more if
+  // x < R % 8) and dealt to the remaining chains in that order, so each of those chains spans as
+  // few XCDs as the round-robin dealing allows.
   const int total = S * H * NS;
+  const int full = total / (8 * NS) * (8 * NS);
   const int wg = blockIdx.x;
   int chain, slice;
-  if (total % (8 * NS) == 0) {
+  if (wg < full) {
     const int loc = wg >> 3;
     slice = loc % NS;
     chain = (loc / NS) * 8 + (wg & 7);
   } else {
-    chain = wg / NS;
-    slice = wg % NS;
+    const int r = wg - full, R = total - full;
+    const int x = r & 7, per = R >> 3, rem = R & 7;
+    const int pos = x * per + (x < rem ? x : rem) + (r >> 3);
+    chain = full / NS + pos / NS;
+    slice = pos % NS;
   }
   const int seq = chain / H, h = chain % H;
   Chain c;
-  c.q = q;
-  c.k = k;
-  c.v = v;
-  c.out = out;
-  c.tok0 = cu ? (int64_t)cu[seq] : 0;
+  const int64_t tok0 = cu ? (int64_t)cu[seq] : 0;
   const int64_t tok1 = cu ? (int64_t)cu[seq + 1] : T;
-  c.n = tok1 > c.tok0 ? tok1 - c.tok0 : 0;
+  const int64_t first = (tok0 * H + h) * D;  // element offset of (tok0, h, 0)
+  c.q = (const char *)(q + first);
+  c.k = (const char *)(k + first);
+  c.v = (const char *)(v + first);
+  c.n = tok1 > tok0 ? tok1 - tok0 : 0;
   c.nb = (int)((c.n + BLK - 1) / BLK);
-  c.H = H;
-  c.h = h;
+  c.b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
+  c.rowbytes = (uint32_t)H * D * 2;
   c.c0 = slice * CV;
   c.slice = slice;
-  c.rev = flags & 1;
+  c.out = (char *)(out + first + c.c0);
   c.incl = flags & 2;
   c.s0t = flags & 4;
 
@@ -611,24 +734,24 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   const int lane = tid & 63;
   switch (tid >> 6) {
-    case 0: output_wave<D, 0, SO>(c, smem, pw, lane); break;
-    case 1: output_wave<D, 1, SO>(c, smem, pw, lane); break;
-    case 2: output_wave<D, 2, SO>(c, smem, pw, lane); break;
-    case 3: output_wave<D, 3, SO>(c, smem, pw, lane); break;
-    case 4: state_wave<D, 0, SO>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 5: state_wave<D, 1, SO>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 6: state_wave<D, 2, SO>(c, smem, pw, s0, fs, sbase, lane); break;
-    default: state_wave<D, 3, SO>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 0: output_wave<D, 0, SO, REV>(c, smem, pw, lane); break;
+    case 1: output_wave<D, 1, SO, REV>(c, smem, pw, lane); break;
+    case 2: output_wave<D, 2, SO, REV>(c, smem, pw, lane); break;
+    case 3: output_wave<D, 3, SO, REV>(c, smem, pw, lane); break;
+    case 4: state_wave<D, 0, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 5: state_wave<D, 1, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 6: state_wave<D, 2, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
+    default: state_wave<D, 3, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
   }
 }
 
-template <int D, bool SO>
+template <int D, bool SO, bool REV>
 hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   const int NS = D / CV;
   const long long grid = (long long)a.S * a.H * NS;
   if (grid <= 0) return hipSuccess;
-  const int flags = (a.reverse ? 1 : 0) | (a.init_inclusive ? 2 : 0) | (a.init_transposed ? 4 : 0);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, SO>), dim3((unsigned)grid), dim3(NTHR), 0, stream,
+  const int flags = (a.init_inclusive ? 2 : 0) | (a.init_transposed ? 4 : 0);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, SO, REV>), dim3((unsigned)grid), dim3(NTHR), 0, stream,
                      (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, a.decay,
                      a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state, a.T, a.S,
                      a.H, flags);
@@ -638,6 +761,10 @@ hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t la_launch_prefill_bf16(const LaPrefillArgs &a, hipStream_t stream) {
-  if (a.state_only) return a.D == 128 ? launch<128, true>(a, stream) : launch<64, true>(a, stream);
-  return a.D == 128 ? launch<128, false>(a, stream) : launch<64, false>(a, stream);
+  if (a.state_only && a.reverse) return hipErrorInvalidValue;  // not instantiated (unused)
+  if (a.state_only)
+    return a.D == 128 ? launch<128, true, false>(a, stream) : launch<64, true, false>(a, stream);
+  if (a.reverse)
+    return a.D == 128 ? launch<128, false, true>(a, stream) : launch<64, false, true>(a, stream);
+  return a.D == 128 ? launch<128, false, false>(a, stream) : launch<64, false, false>(a, stream);
 }
