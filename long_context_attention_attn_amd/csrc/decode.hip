@@ -7,9 +7,9 @@
 // The step is HBM-bound (each 64 KiB state is read once and written once for ~5 d^2 flops),
 // so the kernel is a streaming pass: one workgroup per (sequence, head); a wave reads two
 // (D=128) or four (D=64) consecutive state rows per 128-bit load instruction (1 KiB
-// contiguous), updates them in registers, writes them back with non-temporal stores and
-// accumulates q[a] S'[a][:] for its rows; the per-row-group partial outputs are reduced
-// through LDS.
+// contiguous), all of a thread's rows at once and before waiting for anything else, updates
+// them in registers, writes them back with non-temporal stores and accumulates q[a] S'[a][:]
+// for its rows; the per-row-group partial outputs are reduced through LDS.
 #include "la_internal.h"
 
 namespace {
@@ -51,16 +51,21 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(const T *__restrict__ q,
     vs[tid] = ld<T>(v, vbase + tid);
   }
   const float lam = decay[h];
+  // The state block of this thread (ROWS rows x 4 columns) is requested before the barrier, so
+  // all of its loads are in flight while q, k and v are staged.
+  const int cq = tid % QUADS, rg = tid / QUADS;
+  f32x4 *S4 = (f32x4 *)(state + (size_t)bh * D * D);
+  f32x4 st[ROWS];
+#pragma unroll
+  for (int m = 0; m < ROWS; ++m) st[m] = __builtin_nontemporal_load(S4 + (rg + RG * m) * QUADS + cq);
   __syncthreads();
 
-  const int cq = tid % QUADS, rg = tid / QUADS;
   const f32x4 vv = {vs[4 * cq], vs[4 * cq + 1], vs[4 * cq + 2], vs[4 * cq + 3]};
-  f32x4 *S4 = (f32x4 *)(state + (size_t)bh * D * D);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < ROWS; ++m) {
     const int a = rg + RG * m;
-    f32x4 s = __builtin_nontemporal_load(S4 + a * QUADS + cq);
+    f32x4 s = st[m];
     const float ka = ks[a], qa = qs[a];
     s.x = fmaf(lam, s.x, ka * vv.x);
     s.y = fmaf(lam, s.y, ka * vv.y);
