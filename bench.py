@@ -157,7 +157,7 @@ def main():
             "pct_hbm_peak": 100.0 * dec_gbps / HBM_PEAK_GBPS, "bytes_per_launch": db,
         },
         "roofline": {
-            "bound": "hbm", "kernel": "prefill_bf16_kernel<128>",
+            "bound": "hbm", "kernel": "prefill_bf16_kernel<128, false, false>",
             "achieved": pre_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": pre_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
         },

@@ -325,7 +325,8 @@ __device__ __forceinline__ void dma_rows(const char *base, const Span &s, const 
 }
 
 // L2 prefetch of block rows 16s..16s+15 (s = this workgroup's value slice) of q, k and the full
-// v rows, several blocks before their DMA: one 16-byte read per 128-byte line, written to a
+// v rows, two blocks before their DMA (farther ahead, the 4 MB L2 of an XCD evicts prefetched
+// lines before their use, measured): one 16-byte read per 128-byte line, written to a
 // scratch area of LDS that nothing reads.  The D/32 slices of a head together cover all 64 rows
 // once, and the later DMAs of all four slices then hit L2 instead of waiting on HBM.
 template <int D, bool REV>
@@ -346,7 +347,7 @@ __device__ __forceinline__ void prefetch_l2(const Chain &c, int blk, uint32_t of
 // prefetch instructions per block (no Q when only the state is computed)
 template <bool SO>
 constexpr int pf_dma() { return SO ? 2 : 3; }
-constexpr int PF_AHEAD = 4; // blocks between a block's prefetch and its DMA
+constexpr int PF_AHEAD = 2; // blocks between a block's prefetch and its DMA
 
 // ------------------------------------------------------------------------------------------
 // Output wave r: rows 16r..16r+15 of every block.  The loading duties are dealt against the
