@@ -323,14 +323,24 @@ def cpu_baseline(q, k, v, wl, n_tok, tokens_per_step):
     from oracle import _f64  # noqa: PLC0415
 
     qf, kf, vf = _f64(qs), _f64(ks), _f64(vs)
+    threads = o.num_threads()
     t0 = time.perf_counter()
     o.recurrent(qf, kf, vf, decay.double().numpy())
     dt = time.perf_counter() - t0
+    # One thread on 4 heads of the same tokens (1/16 of the work), scaled to all 64 heads.
+    heads1 = 4
+    o.set_num_threads(1)
+    t1 = time.perf_counter()
+    o.recurrent(qf[:, :heads1], kf[:, :heads1], vf[:, :heads1], decay[:heads1].double().numpy())
+    dt1 = (time.perf_counter() - t1) * (qf.shape[1] / heads1)
+    o.set_num_threads(threads)
     return {
-        "value": n_tok / dt, "unit": "tokens/s", "cores": o.num_threads(), "kind": "oracle",
+        "value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": "recurrent fp64 form on the first %d of 65536 tokens, all 64 heads "
                   "(prefill only; %.1f s)" % (n_tok, dt),
         "seconds": dt,
+        "single_thread": {"value": n_tok / dt1, "unit": "tokens/s", "cores": 1,
+                          "sample": "same tokens, heads 0-3, scaled x16 to 64 heads"},
         "cpu_model": _cpu_model(),
     }
 

@@ -70,6 +70,8 @@ def _bind(lib):
         getattr(lib, name).argtypes = [_DP, _DP, _DP, _DP, _IP, i32, i64, i32, i32, _DP, _DP, _DP,
                                        _DP, _DP, _DP, _DP]
     lib.lao_num_threads.argtypes = []
+    lib.lao_set_num_threads.argtypes = [ctypes.c_int]
+    lib.lao_set_num_threads.restype = None
     for name in ("lao_quadratic", "lao_quadratic_rows", "lao_recurrent", "lao_final_state",
                  "lao_decode_step", "lao_unmasked_left", "lao_unmasked_right",
                  "lao_backward", "lao_backward_recurrent", "lao_num_threads"):
@@ -224,6 +226,10 @@ class Oracle:
     def num_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.lao_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads for the oracle's later parallel loops."""
+        self.lib.lao_set_num_threads(int(n))
 
 
 _default = None

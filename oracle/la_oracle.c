@@ -471,3 +471,11 @@ int lao_num_threads(void) {
   return 1;
 #endif
 }
+
+void lao_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

@@ -112,6 +112,9 @@ int lao_backward_recurrent(const double *q, const double *k, const double *v,
 /* Number of OpenMP threads a parallel region of this library uses (1 without OpenMP). */
 int lao_num_threads(void);
 
+/* Threads later parallel regions use (n >= 1; ignored without OpenMP). */
+void lao_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif
