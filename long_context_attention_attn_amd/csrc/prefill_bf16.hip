@@ -35,7 +35,17 @@
 //   * q/k/v blocks go straight from HBM into LDS (buffer_load ... lds), two blocks ahead of
 //     the one being computed, in a three-stage ring with explicit waits; one barrier per
 //     block.  Buffer range checking zero-fills rows past the end of a sequence and drops
-//     stores past it, so there are no branches around memory operations.
+//     stores past it, so there are no branches around memory operations.  Output waves 0-2
+//     issue the Q and V loads, each state wave its K rows, and the last state wave also pulls
+//     each block's lines into L2 two blocks before their loads (sparse loads into a scratch
+//     area of LDS), so those loads hit L2.
+//
+// Variants of the same scan, used by the sequence-split prefill and by the backward pass:
+// a reversed scan (template REV: local token t is physical token n-1-t of the sequence, for the
+// anti-causal gradients), an initial state that counts as already containing token -1's decay
+// (weight lambda^t at local token t, final state times lambda), a transposed initial state, and
+// a state-only instance (template SO: no Q loads, no outputs) that returns each chain's final
+// state.
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l (g = l/16, c = l%16) holds A[c][k in K(g)],
 // B[k in K(g)][c] and C[4g+i][c], i = 0..3; any k-assignment K(g) shared by A and B gives

@@ -214,3 +214,22 @@ def test_single_head_lengths(n):
     ref = oracle.quadratic(q, k, v, decay)
     assert slice_errors(to_np(out), ref, [0, n]).max() <= BF16_TOL
     assert state_errors(to_np(fs), oracle.final_state(k, v, decay)).max() <= BF16_TOL
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_workgroup_mapping_with_tail(D):
+    """63 heads x 3 sequences: the workgroup count is not a multiple of 8 x slices, so most
+    chains take the XCD-grouped order and the rest the tail order; every row against O1."""
+    banner("mapping tail H=63 S=3 D=%d" % D)
+    lengths = [70, 1, 130]
+    H = 63
+    cu = synth.cu_from_lengths(lengths)
+    q, k, v = synth.qkv(int(cu[-1]), H, D, torch.bfloat16, seed=40)
+    decay = synth.decay_geometric(H, 0.8, 0.999)
+    out, fs = _run_prefill(q, k, v, decay, cu)
+    ref = oracle.quadratic(q, k, v, decay, cu)
+    ref_s = oracle.final_state(k, v, decay, cu)
+    e = slice_errors(to_np(out), ref, cu)
+    es = state_errors(to_np(fs), ref_s)
+    print("mapping tail: out %.2e state %.2e" % (e.max(), es.max()))
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
