@@ -104,3 +104,23 @@ def test_decode_256x64():
     es = float(np.abs(to_np(st) - ref_s).max() / np.abs(ref_s).max())
     print("decode_256x64: out %.2e state(max-abs rel) %.2e" % (e, es))
     assert e <= BF16_TOL and es <= 1e-6
+
+
+def test_prefill_64k_d64_all_heads():
+    """65,536 tokens x 16 heads x d64 (bf16, GPU inputs): every head against the recurrent form,
+    plus sampled rows against the quadratic form."""
+    banner("prefill T=65536 H=16 D=64 bf16 (GPU inputs)")
+    T, H, D = 65536, 16, 64
+    q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=7, device="cuda")
+    decay = synth.decay_geometric(H, 0.9, 0.9999)
+    out, fs = la.prefill(q, k, v, decay.to(dev()))
+    torch.cuda.synchronize()
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    ref, ref_s = oracle.recurrent(qc, kc, vc, decay)
+    e = slice_errors(to_np(out), ref, [0, T])
+    es = state_errors(to_np(fs), ref_s)
+    rows = [0, 63, 64, 4097, T - 1]
+    er = max(rel(to_np(out[rows])[:, h], oracle.quadratic_rows(qc, kc, vc, decay, rows)[:, h])
+             for h in range(H))
+    print("prefill d64: out %.2e state %.2e rows %.2e" % (e.max(), es.max(), er))
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL and er <= BF16_TOL
