@@ -31,8 +31,9 @@
  * (fp32 storage and arithmetic).  Devices: gfx950 only.
  *
  * Ownership and memory.  The caller owns every buffer; the library keeps no pointer after a
- * call returns and allocates no device memory.  out must not alias q, k or v; state buffers
- * must not alias anything else.
+ * call returns and allocates no device memory.  out must not overlap q, k or v; state buffers
+ * must not overlap each other or the activations.  The host checks these byte ranges (from the
+ * sizes given) and returns LA_ERR_INVALID_ARG on an overlap; q, k and v may share memory.
  *
  * Errors.  Argument checks run on the host before any HIP call and return a status; nothing
  * throws across this ABI.  Device data is not validated: non-monotone cu_seqlens or lambda

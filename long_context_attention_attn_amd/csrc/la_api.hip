@@ -26,6 +26,33 @@ la_status fail(la_status s, const char *fmt, ...) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether the byte ranges [a, a + na) and [b, b + nb) intersect (empty ranges never do).
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t elem_bytes(la_dtype dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+// out must not overlap q, k or v ([n][H][D] each); state buffers ([S][H][D][D] fp32) must not
+// overlap each other or the activations.
+la_status check_aliasing(const void *q, const void *k, const void *v, const void *out,
+                         int64_t n, const float *st_a, const float *st_b, int64_t nst, int32_t H,
+                         int32_t D, la_dtype dtype) {
+  const size_t act = (size_t)n * H * D * elem_bytes(dtype);
+  const size_t st = (size_t)nst * H * D * D * sizeof(float);
+  const void *in[3] = {q, k, v};
+  for (const void *x : in)
+    if (overlaps(out, act, x, act)) return fail(LA_ERR_INVALID_ARG, "out overlaps q, k or v");
+  const void *acts[4] = {q, k, v, out};
+  for (const float *s : {st_a, st_b})
+    for (const void *x : acts)
+      if (overlaps(s, st, x, act)) return fail(LA_ERR_INVALID_ARG, "a state buffer overlaps an activation");
+  if (overlaps(st_a, st, st_b, st)) return fail(LA_ERR_INVALID_ARG, "state buffers overlap");
+  return LA_OK;
+}
+
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];   // 1 = gfx950, 0 = other arch
@@ -124,6 +151,8 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
   if ((long long)S * H * (D / 32) > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "S*H too large");
   if (initial_state != nullptr && initial_state == final_state)
     return fail(LA_ERR_INVALID_ARG, "initial_state aliases final_state");
+  st = check_aliasing(q, k, v, out, T, initial_state, final_state, S, H, D, dtype);
+  if (st != LA_OK) return st;
   if (final_state == nullptr && (T == 0)) return LA_OK;  // nothing to compute or write
   st = check_device();
   if (st != LA_OK) return st;
@@ -187,6 +216,8 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   if (initial_state != nullptr && initial_state == final_state)
     return fail(LA_ERR_INVALID_ARG, "initial_state aliases final_state");
   if (seg_blocks < 1) return fail(LA_ERR_INVALID_ARG, "seg_blocks = %d < 1", seg_blocks);
+  st = check_aliasing(q, k, v, out, T, initial_state, final_state, S, H, D, dtype);
+  if (st != LA_OK) return st;
   if (T > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "split prefill needs T < 2^31");
   if (T == 0)  // no segments: final states are the initial states (or zeros)
     return la_prefill_ex(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H,
@@ -200,6 +231,17 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   if (workspace_bytes < lay.bytes)
     return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
                 lay.bytes);
+  {
+    const size_t act = (size_t)T * H * D * elem_bytes(dtype);
+    const size_t stb = (size_t)S * H * D * D * sizeof(float);
+    if (overlaps(workspace, lay.bytes, q, act) || overlaps(workspace, lay.bytes, k, act) ||
+        overlaps(workspace, lay.bytes, v, act) || overlaps(workspace, lay.bytes, out, act) ||
+        overlaps(workspace, lay.bytes, initial_state, stb) ||
+        overlaps(workspace, lay.bytes, final_state, stb) ||
+        overlaps(workspace, lay.bytes, decay, (size_t)H * sizeof(float)) ||
+        overlaps(workspace, lay.bytes, cu_seqlens, (size_t)(S + 1) * sizeof(int32_t)))
+      return fail(LA_ERR_INVALID_ARG, "workspace overlaps an argument buffer");
+  }
   st = check_device();
   if (st != LA_OK) return st;
 
@@ -253,22 +295,26 @@ la_status la_backward(const void *q, const void *k, const void *v, const float *
     if (!dq || !dk || !dv) return fail(LA_ERR_INVALID_ARG, "dq, dk or dv is NULL");
     if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
       return fail(LA_ERR_INVALID_ARG, "dq, dk and dv must be 16-byte aligned");
+    const size_t act = (size_t)T * H * D * elem_bytes(dtype);
     const void *in[4] = {q, k, v, d_out};
     const void *grad[3] = {dq, dk, dv};
     for (const void *g : grad) {
       for (const void *x : in)
-        if (g == x) return fail(LA_ERR_INVALID_ARG, "a gradient output aliases an input");
+        if (overlaps(g, act, x, act)) return fail(LA_ERR_INVALID_ARG, "a gradient output overlaps an input");
     }
-    if (dq == dk || dq == dv || dk == dv)
-      return fail(LA_ERR_INVALID_ARG, "dq, dk and dv must be distinct");
+    if (overlaps(dq, act, dk, act) || overlaps(dq, act, dv, act) || overlaps(dk, act, dv, act))
+      return fail(LA_ERR_INVALID_ARG, "dq, dk and dv must not overlap");
   }
   if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
   if (cu_seqlens == nullptr && S != 1)
     return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
   if ((long long)S * H * (D / 32) > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "S*H too large");
-  if (d_initial_state != nullptr &&
-      (d_initial_state == initial_state || d_initial_state == d_final_state))
-    return fail(LA_ERR_INVALID_ARG, "d_initial_state aliases a state input");
+  {
+    const size_t stb = (size_t)S * H * D * D * sizeof(float);
+    if (overlaps(d_initial_state, stb, initial_state, stb) ||
+        overlaps(d_initial_state, stb, d_final_state, stb))
+      return fail(LA_ERR_INVALID_ARG, "d_initial_state overlaps a state input");
+  }
   if (T == 0 && d_initial_state == nullptr) return LA_OK;
   st = check_device();
   if (st != LA_OK) return st;
@@ -333,6 +379,8 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const floa
   if (state == nullptr) return fail(LA_ERR_INVALID_ARG, "state is NULL");
   if (!aligned16(state)) return fail(LA_ERR_INVALID_ARG, "state must be 16-byte aligned");
   if ((long long)Bt * H > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "Bt*H too large");
+  st = check_aliasing(q, k, v, out, Bt, state, nullptr, Bt, H, D, dtype);
+  if (st != LA_OK) return st;
   st = check_device();
   if (st != LA_OK) return st;
   LaDecodeArgs a;
@@ -363,6 +411,15 @@ la_status la_decode_tokens(const void *q, const void *k, const void *v, const fl
   if (state == nullptr) return fail(LA_ERR_INVALID_ARG, "state is NULL");
   if (!aligned16(state)) return fail(LA_ERR_INVALID_ARG, "state must be 16-byte aligned");
   if ((long long)Bt * H > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "Bt*H too large");
+  {
+    const size_t act = (size_t)Bt * m * H * D * elem_bytes(dtype);
+    const size_t stb = (size_t)Bt * H * D * D * sizeof(float);
+    const void *acts[4] = {q, k, v, out};
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(out, act, acts[i], act)) return fail(LA_ERR_INVALID_ARG, "out overlaps q, k or v");
+    for (const void *x : acts)
+      if (overlaps(state, stb, x, act)) return fail(LA_ERR_INVALID_ARG, "state overlaps an activation");
+  }
   st = check_device();
   if (st != LA_OK) return st;
   LaDecodeArgs a;

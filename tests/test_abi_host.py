@@ -53,6 +53,7 @@ def test_version_and_status_strings(lib):
 P = ctypes.c_void_p(0x100000)
 P2 = ctypes.c_void_p(0x200000)
 MISALIGNED = ctypes.c_void_p(0x100008)
+OUT = ctypes.c_void_p(0x700000)
 
 
 def _prefill(lib, q=P, k=P, v=P, decay=P, cu=None, out=P2, fs=None, T=64, S=1, H=2, D=128,
@@ -65,6 +66,10 @@ def _prefill(lib, q=P, k=P, v=P, decay=P, cu=None, out=P2, fs=None, T=64, S=1, H
     (dict(H=0), 1), (dict(T=-1), 1), (dict(S=0), 1), (dict(S=2), 1),  # S=2 without cu_seqlens
     (dict(q=None), 1), (dict(out=None), 1), (dict(decay=None), 1),
     (dict(q=MISALIGNED), 1), (dict(init=P2, fs=P2), 1),
+    # byte-range overlaps: q, k, v are 64 x 2 x 128 bf16 = 32 KiB, states 2 x 64 KiB
+    (dict(out=ctypes.c_void_p(0x100000 + 0x7ff0)), 1), (dict(v=ctypes.c_void_p(0x200000 - 0x10)), 1),
+    (dict(fs=ctypes.c_void_p(0x204000)), 1), (dict(init=ctypes.c_void_p(0x100010)), 1),
+    (dict(init=ctypes.c_void_p(0x300000), fs=ctypes.c_void_p(0x310000)), 1),
 ])
 def test_prefill_validation(lib, kwargs, status):
     assert _prefill(lib, **kwargs) == status
@@ -81,7 +86,7 @@ def test_prefill_empty_is_noop(lib):
     (dict(state=MISALIGNED), 1), (dict(q=None), 1),
 ])
 def test_decode_validation(lib, kwargs, status):
-    a = dict(q=P, k=P, v=P, decay=P, state=P2, out=P, Bt=4, H=2, D=128, dt=1)
+    a = dict(q=P, k=P, v=P, decay=P, state=P2, out=OUT, Bt=4, H=2, D=128, dt=1)
     a.update(kwargs)
     rc = lib.la_decode_step(a["q"], a["k"], a["v"], a["decay"], a["state"], a["out"], a["Bt"],
                             a["H"], a["D"], a["dt"], None)
@@ -187,8 +192,53 @@ def test_backward_without_device(lib):
     (dict(state=MISALIGNED), 1), (dict(D=100), 2), (dict(q=None), 1),
 ])
 def test_decode_tokens_validation(lib, kwargs, status):
-    a = dict(q=P, k=P, v=P, decay=P, state=P2, out=P, Bt=4, m=3, H=2, D=128, dt=1)
+    a = dict(q=P, k=P, v=P, decay=P, state=P2, out=OUT, Bt=4, m=3, H=2, D=128, dt=1)
     a.update(kwargs)
     rc = lib.la_decode_tokens(a["q"], a["k"], a["v"], a["decay"], a["state"], a["out"], a["Bt"],
                               a["m"], a["H"], a["D"], a["dt"], None)
     assert rc == status
+
+
+def test_adjacent_buffers_are_not_overlaps(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    # out starts right after q ends; states back to back: validation passes, the device check
+    # (no GPU here) reports the HIP error.
+    end = 0x100000 + 64 * 2 * 128 * 2
+    assert _prefill(lib, out=ctypes.c_void_p(end), init=ctypes.c_void_p(0x300000),
+                    fs=ctypes.c_void_p(0x300000 + 2 * 128 * 128 * 4)) == 3
+    rc = lib.la_decode_step(P, P, P, P, P2, ctypes.c_void_p(0x100000 + 4 * 2 * 128 * 2), 4, 2,
+                            128, 1, None)
+    assert rc == 3
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(out=ctypes.c_void_p(0x100100)), dict(state=ctypes.c_void_p(0x700000)),
+    dict(state=ctypes.c_void_p(0x100000 - 0x10)),
+])
+def test_decode_overlap_rejected(lib, kwargs):
+    a = dict(q=P, k=P, v=P, state=P2, out=OUT)
+    a.update(kwargs)
+    assert lib.la_decode_step(a["q"], a["k"], a["v"], P, a["state"], a["out"], 4, 2, 128, 1,
+                              None) == 1
+    assert b"overlap" in lib.la_last_error()
+    assert lib.la_decode_tokens(a["q"], a["k"], a["v"], P, a["state"], a["out"], 4, 3, 2, 128, 1,
+                                None) == 1
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(dq=ctypes.c_void_p(0x200000 + 0x4000)), dict(dv=ctypes.c_void_p(0x500000 + 0x7f00)),
+    dict(dk=ctypes.c_void_p(0x100000 + 0x10)),
+])
+def test_backward_overlap_rejected(lib, kwargs):
+    assert _backward(lib, **kwargs) == 1
+    assert b"overlap" in lib.la_last_error()
+
+
+@pytest.mark.parametrize("ws", [0x100000, 0x200000 - 0x100, 0x700000])
+def test_split_workspace_overlap_rejected(lib, ws):
+    # a workspace that overlaps q (at P), out (at P2) or the final states (at 0x700000)
+    assert _split(lib, ws=ctypes.c_void_p(ws), fs=ctypes.c_void_p(0x700000)) == 1
+    assert b"overlap" in lib.la_last_error()
