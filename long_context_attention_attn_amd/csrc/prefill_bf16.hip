@@ -76,16 +76,20 @@ struct Cfg {
   static constexpr int QK_DMA = 16 / RPI;                  // DMA instructions per 16 rows
   static constexpr int KSTEPS = D / 32;                    // MFMA k-steps over features
   static constexpr int VROWB = 2 * CV;                     // bytes per V row
+  // A stage holds everything one block needs: its Q, K and V rows (DMA targets), the bf16 copy
+  // of the state it starts from and its decayed V rows.  Every LDS address in the block loop is
+  // then a per-block base (one per lane pattern) plus an immediate below 64 KiB.
   static constexpr int Q_OFF = 0;                          // byte offsets inside a stage
   static constexpr int K_OFF = BLK * ROWB;
   static constexpr int V_OFF = 2 * BLK * ROWB;
-  static constexpr int STAGE = 2 * BLK * ROWB + BLK * VROWB;
   static constexpr int KVX = CV * ROWB;                    // bf16 state copy [CV][D]
-  static constexpr int KVX_OFF = NST * STAGE;
+  static constexpr int KVX_OFF = V_OFF + BLK * VROWB;
   static constexpr int LV = BLK * VROWB;                   // decayed V copy, [BLK][CV]
-  static constexpr int LV_OFF = NST * STAGE + 2 * KVX;
-  static constexpr int PF_OFF = LV_OFF + 2 * LV;           // 1 KiB sink of the L2 prefetches
+  static constexpr int LV_OFF = KVX_OFF + KVX;
+  static constexpr int STAGE = LV_OFF + LV;
+  static constexpr int PF_OFF = NST * STAGE;               // 1 KiB sink of the L2 prefetches
   static constexpr int SMEM = PF_OFF + 1024;
+  static_assert(STAGE < 65536, "stage offsets must fit the LDS instruction offset");
 };
 
 // State rows owned by state wave R (in 16-row tiles) and its first row.  Output wave r does
@@ -367,8 +371,8 @@ constexpr int PF_AHEAD = 2; // blocks between a block's prefetch and its DMA
 // score work (wave r does r+1 score tiles): wave 0 loads Q rows 0..15 and V rows 0..31, wave 1
 // Q rows 16..31 and 48..63 and V rows 32..47, wave 2 Q rows 32..47 and V rows 48..63, wave 3
 // (four score tiles) nothing.  Once its V rows of the next block have landed, a wave writes them
-// decayed, lambda^(b-1-j) V[j], to the double-buffered copy the state waves consume (so no state
-// wave scales operands).
+// decayed, lambda^(b-1-j) V[j], to that block's stage, where the state waves consume it (so no
+// state wave scales operands).
 // ------------------------------------------------------------------------------------------
 template <int D, int R, bool SO, bool REV>
 __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const float *pw,
@@ -428,8 +432,19 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
     lv_last[m] = vrow < b_last ? pw[b_last - 1 - vrow] : 0.f;
   }
 
-  auto issue = [&](int blk) {
-    const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
+  // Lane parts of this wave's LDS addresses; each block adds its stage offset once per pattern
+  // (kept opaque to the compiler) and every access adds an immediate.  Rows 16 x + l16 of a
+  // swizzled [rows][D] tile share the pattern of row l16 (the swizzle depends on row mod 8 and
+  // bit 2); V rows 16 x + trow share that of row trow.
+  uint32_t kpat[C::KSTEPS], vpat[2];
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) kpat[ks] = (uint32_t)swz<D>(l16, 32 * ks + 8 * g);
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) vpat[ct] = (uint32_t)vswz(trow, 16 * ct + tcol);
+  const uint32_t dpat = (uint32_t)((16 * VG0 + lane / 4) * C::VROWB + 16 * (lane % 4));
+
+  auto issue = [&](int blk, uint32_t st_off) {
+    const uint32_t st = smem_lds + st_off;
     const Span sp = span<REV>(c, blk);
     if constexpr (!SO && R < 3)
       dma_rows<D, REV>(c.q, sp, qoff[0], st + C::Q_OFF + 16 * R * C::ROWB);
@@ -441,42 +456,52 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
     else if constexpr (NVG == 1)
       dma16(rsrc(vslice + sp.off, sp.bytes), at<REV>(sp, voff[0]), vl);
   };
-  // Decayed copy of this wave's V rows of block blk (landed) into buffer blk & 1.  All reads
-  // are issued before any write, so the LDS round trips overlap.
-  auto decay_v = [&](int blk) {
+  // Decayed copy of this wave's V rows of block blk (landed in the stage at st_off) into the same
+  // stage.  All reads are issued before any write, so the LDS round trips overlap.
+  auto decay_v = [&](int blk, uint32_t st_off) {
     if constexpr (NVG > 0) {
       const bool last = blk == c.nb - 1;
+      uint32_t db = dpat + st_off;
+      asm volatile("" : "+v"(db));
       bf16x8 x[NVG];
 #pragma unroll
       for (int m = 0; m < NVG; ++m)
-        x[m] = *(const bf16x8 *)(smem + (blk % NST) * C::STAGE + C::V_OFF +
-                                 (16 * (VG0 + m) + lane / 4) * C::VROWB + 16 * (lane % 4));
+        x[m] = *(const bf16x8 *)(smem + db + (C::V_OFF + 16 * m * C::VROWB));
 #pragma unroll
       for (int m = 0; m < NVG; ++m)
-        *(bf16x8 *)(smem + C::LV_OFF + (blk & 1) * C::LV + (16 * (VG0 + m) + lane / 4) * C::VROWB +
-                    16 * (lane % 4)) = scale8(x[m], last ? lv_last[m] : lv_full[m]);
+        *(bf16x8 *)(smem + db + (C::LV_OFF + 16 * m * C::VROWB)) =
+            scale8(x[m], last ? lv_last[m] : lv_full[m]);
     }
   };
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s);
+  static_assert(NST == 3, "stage rotation and wait counts are written for three stages");
+  // Stage offsets of blocks i (cur), i + 1 (nxt) and i + 2 (prv: the stage read in step i - 1).
+  uint32_t s_cur = 0, s_nxt = C::STAGE, s_prv = 2 * C::STAGE;
+  issue(0, 0);
+  issue(1, C::STAGE);
   if constexpr (DMA > 0) wait_vm<(NST - 2) * DMA>();  // own block-0 rows landed
-  decay_v(0);
+  decay_v(0, 0);
   lds_barrier();  // block 0 and its decayed V visible to all waves
 
   for (int i = 0; i < c.nb; ++i) {
-    issue(i + NST - 1);  // refills the stage read in step i-1
+    issue(i + NST - 1, s_prv);  // refills the stage read in step i-1
     if constexpr (!SO) {
-      const char *stage = smem + (i % NST) * C::STAGE;
-      const char *Qs = stage + C::Q_OFF;
-      const char *Ks = stage + C::K_OFF;
-      const char *Vs = stage + C::V_OFF;
-      const char *KVs = smem + C::KVX_OFF + (i & 1) * C::KVX;
+      uint32_t kb[C::KSTEPS], vb[2];
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        kb[ks] = kpat[ks] + s_cur;
+        asm volatile("" : "+v"(kb[ks]));
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        vb[ct] = vpat[ct] + s_cur;
+        asm volatile("" : "+v"(vb[ct]));
+      }
 
       // Q operand (B of S^T and of the inter product): Q[jrow][32 ks + 8 g + 0..7].
       bf16x8 qop[C::KSTEPS];
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks)
-        qop[ks] = *(const bf16x8 *)(Qs + swz<D>(jrow, 32 * ks + 8 * g));
+        qop[ks] = *(const bf16x8 *)(smem + kb[ks] + (C::Q_OFF + 16 * R * C::ROWB));
 
       // S^T[16t + 4g + i][jrow] = P[jrow][16t + 4g + i] before masking.
       f32x4 sacc[NT];
@@ -486,8 +511,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          sacc[t] = mfma(*(const bf16x8 *)(Ks + swz<D>(16 * t + l16, 32 * ks + 8 * g)), qop[ks],
-                         sacc[t]);
+          sacc[t] = mfma(*(const bf16x8 *)(smem + kb[ks] + (C::K_OFF + 16 * t * C::ROWB)),
+                         qop[ks], sacc[t]);
 
       // Inter part: O^T[16ct + 4g + i][jrow] = sum_dk KV[dk][16ct + 4g + i] Q[jrow][dk].
       f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -495,8 +520,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-          o[ct] = mfma(*(const bf16x8 *)(KVs + swz<D>(16 * ct + l16, 32 * ks + 8 * g)), qop[ks],
-                       o[ct]);
+          o[ct] = mfma(*(const bf16x8 *)(smem + kb[ks] + (C::KVX_OFF + 16 * ct * C::ROWB)),
+                       qop[ks], o[ct]);
 
       // V operands of the causal k-steps: lane (g, c) = V[32s + {4g+e, 16+4g+e}][16ct + c].
       bf16x8 vop[NS][2];
@@ -504,8 +529,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const bf16x4 lo = tr_read(Vs + vswz(32 * s + trow, 16 * ct + tcol));
-          const bf16x4 hi = tr_read(Vs + vswz(32 * s + 16 + trow, 16 * ct + tcol));
+          const bf16x4 lo = tr_read(smem + vb[ct] + (C::V_OFF + 32 * s * C::VROWB));
+          const bf16x4 hi = tr_read(smem + vb[ct] + (C::V_OFF + (32 * s + 16) * C::VROWB));
           vop[s][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 
@@ -552,8 +577,12 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       if (i == 0) wait_vm<DMA + STORES>();
       else wait_vm<DMA + 2 * STORES>();
     }
-    decay_v(i + 1);
+    decay_v(i + 1, s_nxt);
     lds_barrier();
+    const uint32_t so = s_cur;
+    s_cur = s_nxt;
+    s_nxt = s_prv;
+    s_prv = so;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // DMAs in flight target this LDS
 }
@@ -589,14 +618,29 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
         const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
         kv[rt][ct][i] = s0 ? s0[sbase + (c.s0t ? (size_t)dv * D + dk : (size_t)dk * D + dv)] : 0.f;
       }
-  auto write_kvx = [&](char *dst) {
+  const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
+  // Lane parts of the LDS addresses (see the output waves): state copy rows 16 ct + l16, K rows
+  // 16 x + trow (transpose reads), decayed V rows 16 x + trow.
+  uint32_t xpat[RT > 0 ? RT : 1], kpat[RT > 0 ? RT : 1], vpat[2];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RT; ++rt) {
+    xpat[rt] = (uint32_t)swz<D>(l16, DK0 + 16 * rt + 4 * g);
+    kpat[rt] = (uint32_t)swz<D>(trow, DK0 + 16 * rt + tcol);
+  }
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) vpat[ct] = (uint32_t)vswz(trow, 16 * ct + tcol);
+  // bf16 copy of the state into the stage at st_off, for the inter product of its block
+  auto write_kvx = [&](uint32_t st_off) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      uint32_t xb = xpat[rt] + st_off;
+      asm volatile("" : "+v"(xb));
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        *(bf16x4 *)(dst + swz<D>(16 * ct + l16, DK0 + 16 * rt + 4 * g)) = to_bf16x4(kv[rt][ct]);
+        *(bf16x4 *)(smem + xb + (C::KVX_OFF + 16 * ct * C::ROWB)) = to_bf16x4(kv[rt][ct]);
+    }
   };
-  write_kvx(smem + C::KVX_OFF);
+  write_kvx(0);
 
   // lambda^b for full blocks and for the last block, which may be partial (b_last rows).
   const int b_last = c.b_last;
@@ -607,13 +651,12 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   // Scale of the final state: lambda for an inclusive initial state (read now: the powers
   // table is overwritten by the pipeline's DMAs).
   const float fsc = c.incl && c.nb > 0 ? pw[1] : 1.f;
-  const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
 
   uint32_t koff[C::QK_DMA];
   rows_offsets<D, REV>(R, lane, c.rowbytes, koff);
   const uint32_t pfoff = prefetch_offset<D, REV>(c.slice, lane, c.rowbytes);
-  auto issue = [&](int blk) {
-    const uint32_t st = smem_lds + (uint32_t)((blk % NST) * C::STAGE);
+  auto issue = [&](int blk, uint32_t st_off) {
+    const uint32_t st = smem_lds + st_off;
     dma_rows<D, REV>(c.k, span<REV>(c, blk), koff, st + C::K_OFF + 16 * R * C::ROWB);
     // after the DMA, so that waiting for this DMA never waits for a prefetch (counters are
     // in order)
@@ -624,15 +667,26 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
     for (int blk = NST - 1; blk < PF_AHEAD; ++blk)
       prefetch_l2<SO, REV>(c, blk, pfoff, smem_lds + C::PF_OFF);
   }
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s);
+  static_assert(NST == 3, "stage rotation is written for three stages");
+  uint32_t s_cur = 0, s_nxt = C::STAGE, s_prv = 2 * C::STAGE;
+  issue(0, 0);
+  issue(1, C::STAGE);
   wait_vm_barrier<WAIT>();
 
   for (int i = 0; i < c.nb; ++i) {
-    issue(i + NST - 1);
-    const char *Ks = smem + (i % NST) * C::STAGE + C::K_OFF;
-    const char *LVs = smem + C::LV_OFF + (i & 1) * C::LV;  // lambda^(b-1-j) V[j]
+    issue(i + NST - 1, s_prv);
     if constexpr (RT > 0) {
+      uint32_t kb[RT], vb[2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        kb[rt] = kpat[rt] + s_cur;
+        asm volatile("" : "+v"(kb[rt]));
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        vb[ct] = vpat[ct] + s_cur;
+        asm volatile("" : "+v"(vb[ct]));
+      }
       const float lb = i == 0 ? lb_first : i == c.nb - 1 ? lb_last : lb_full;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -642,25 +696,28 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
       for (int s = 0; s < 2; ++s) {
         bf16x8 vop[2];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const bf16x4 lo = tr_read(LVs + vswz(32 * s + trow, 16 * ct + tcol));
-          const bf16x4 hi = tr_read(LVs + vswz(32 * s + 16 + trow, 16 * ct + tcol));
+        for (int ct = 0; ct < 2; ++ct) {  // lambda^(b-1-j) V[j]
+          const bf16x4 lo = tr_read(smem + vb[ct] + (C::LV_OFF + 32 * s * C::VROWB));
+          const bf16x4 hi = tr_read(smem + vb[ct] + (C::LV_OFF + (32 * s + 16) * C::VROWB));
           vop[ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int col = DK0 + 16 * rt + tcol;
-          const bf16x4 lo = tr_read(Ks + swz<D>(32 * s + trow, col));
-          const bf16x4 hi = tr_read(Ks + swz<D>(32 * s + 16 + trow, col));
+          const bf16x4 lo = tr_read(smem + kb[rt] + (C::K_OFF + 32 * s * C::ROWB));
+          const bf16x4 hi = tr_read(smem + kb[rt] + (C::K_OFF + (32 * s + 16) * C::ROWB));
           const bf16x8 kop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) kv[rt][ct] = mfma(kop, vop[ct], kv[rt][ct]);
         }
       }
-      write_kvx(smem + C::KVX_OFF + ((i + 1) & 1) * C::KVX);
+      write_kvx(s_nxt);
     }
     // Block i+1's K rows landed: since their DMA this wave issued only the later issues.
     wait_vm_barrier<WAIT>();
+    const uint32_t so = s_cur;
+    s_cur = s_nxt;
+    s_nxt = s_prv;
+    s_prv = so;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
