@@ -187,6 +187,40 @@ __device__ __forceinline__ void dma16x4(__amdgpu_buffer_rsrc_t r, uint32_t o0, u
       : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(m0), "s"(m1), "s"(m2), "s"(m3), "s"(r)
       : "memory");
 }
+// Two or four copies into consecutive KiBs of LDS from one M0 value: the instruction offset
+// (k KiB for copy k) is added to both the LDS and the memory address, so the caller passes lane
+// offsets with k KiB already subtracted (they stay non-negative for forward scans, whose copy k
+// starts at least k KiB into the block's range).
+__device__ __forceinline__ void dma_kib2(__amdgpu_buffer_rsrc_t r, uint32_t o0, uint32_t o1,
+                                         uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %4, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %4, 0 offen offset:1024 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "s"(m0), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void dma_kib4(__amdgpu_buffer_rsrc_t r, uint32_t o0, uint32_t o1,
+                                         uint32_t o2, uint32_t o3, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %6, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %6, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %6, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %6, 0 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(m0), "s"(r)
+      : "memory");
+}
 // One offset, one LDS address, two or three descriptors (the L2 prefetches of k, v [and q]).
 __device__ __forceinline__ void dma16_same2(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                             uint32_t o, uint32_t m0) {
@@ -282,6 +316,10 @@ struct Chain {
   int nb;                 // number of blocks
   int b_last;             // rows of the last block
   uint32_t rowbytes;      // bytes per token row of q, k, v, out (H * D * 2)
+  uint32_t full_bytes;    // BLK * rowbytes
+  uint32_t last_bytes;    // b_last * rowbytes
+  uint32_t full_last;     // (BLK - 1) * rowbytes
+  uint32_t last_last;     // (b_last - 1) * rowbytes
   int c0, slice;          // first value column of the slice, c0 / CV
   bool incl;              // initial state weighted lambda^t, final state times lambda
   bool s0t;               // initial state read transposed
@@ -298,12 +336,32 @@ struct Span {
   uint32_t bytes;  // b * rowbytes
   uint32_t last;   // (b - 1) * rowbytes
 };
+// Walk over consecutive blocks: `run` is the range start of block blk if it were full (forward
+// blk * BLK rows, reversed n - (blk + 1) * BLK rows, in bytes) and moves by BLK rows per block,
+// so a block's span costs a few scalar selects.  The last block starts at row (nb - 1) * BLK
+// forward and at row 0 reversed; blocks past the end have an empty range.
+struct Walk {
+  int64_t run;
+  int blk;
+};
 template <bool REV>
-__device__ __forceinline__ Span span(const Chain &c, int blk) {
-  const int b = blk < c.nb - 1 ? BLK : (blk == c.nb - 1 ? c.b_last : 0);
-  int64_t row = 0;
-  if (b > 0) row = REV ? c.n - (int64_t)blk * BLK - b : (int64_t)blk * BLK;
-  return Span{row * (int64_t)c.rowbytes, (uint32_t)b * c.rowbytes, (uint32_t)(b - 1) * c.rowbytes};
+__device__ __forceinline__ Walk walk_from(const Chain &c, int blk) {
+  const int64_t row = REV ? c.n - (int64_t)(blk + 1) * BLK : (int64_t)blk * BLK;
+  return Walk{row * (int64_t)c.rowbytes, blk};
+}
+template <bool REV>
+__device__ __forceinline__ Span span_at(const Chain &c, const Walk &w) {
+  const bool full = w.blk < c.nb - 1;
+  Span s;
+  s.bytes = full ? c.full_bytes : (w.blk == c.nb - 1 ? c.last_bytes : 0u);
+  s.off = (REV && !full) ? 0 : w.run;
+  s.last = full ? c.full_last : c.last_last;
+  return s;
+}
+template <bool REV>
+__device__ __forceinline__ void advance(const Chain &c, Walk &w) {
+  w.run += REV ? -(int64_t)c.full_bytes : (int64_t)c.full_bytes;
+  ++w.blk;
 }
 // Byte offset of byte `col` of local row `row` of a block, in two steps: lane_base once per wave
 // (row * rowbytes + col forward, row * rowbytes - col reversed), then at() per block.
@@ -324,7 +382,9 @@ __device__ __forceinline__ void rows_offsets(int r, int lane, uint32_t rowbytes,
   for (int a = 0; a < C::QK_DMA; ++a) {
     const int row = 16 * r + a * C::RPI + lane / C::CH;
     const int chunk = (lane % C::CH) ^ swf<D>(row);  // lands at position lane % CH
-    offs[a] = lane_base<REV>(row, 16u * chunk, rowbytes);
+    // forward: minus the KiBs the instruction offset adds back (row >= a * RPI and
+    // RPI * rowbytes >= RPI * ROWB = 1 KiB keep it non-negative)
+    offs[a] = lane_base<REV>(row, 16u * chunk, rowbytes) - (REV ? 0u : 1024u * a);
   }
 }
 // DMA rows 16r..16r+15 of a [64][D] tile of the block at span s into LDS address lds (their
@@ -334,11 +394,18 @@ __device__ __forceinline__ void dma_rows(const char *base, const Span &s, const 
                                          uint32_t lds) {
   using C = Cfg<D>;
   const auto rs = rsrc(base + s.off, s.bytes);
-  if constexpr (C::QK_DMA == 4)
-    dma16x4(rs, at<REV>(s, offs[0]), at<REV>(s, offs[1]), at<REV>(s, offs[2]), at<REV>(s, offs[3]),
-            lds, lds + 1024, lds + 2048, lds + 3072);
-  else
-    dma16x2(rs, at<REV>(s, offs[0]), at<REV>(s, offs[1]), lds, lds + 1024);
+  if constexpr (REV) {
+    if constexpr (C::QK_DMA == 4)
+      dma16x4(rs, at<REV>(s, offs[0]), at<REV>(s, offs[1]), at<REV>(s, offs[2]),
+              at<REV>(s, offs[3]), lds, lds + 1024, lds + 2048, lds + 3072);
+    else
+      dma16x2(rs, at<REV>(s, offs[0]), at<REV>(s, offs[1]), lds, lds + 1024);
+  } else {
+    if constexpr (C::QK_DMA == 4)
+      dma_kib4(rs, offs[0], offs[1], offs[2], offs[3], lds);
+    else
+      dma_kib2(rs, offs[0], offs[1], lds);
+  }
 }
 
 // L2 prefetch of block rows 16s..16s+15 (s = this workgroup's value slice) of q, k and the full
@@ -352,8 +419,8 @@ __device__ __forceinline__ uint32_t prefetch_offset(int slice, int lane, uint32_
                         rowbytes);
 }
 template <bool SO, bool REV>
-__device__ __forceinline__ void prefetch_l2(const Chain &c, int blk, uint32_t off, uint32_t sink) {
-  const Span s = span<REV>(c, blk);
+__device__ __forceinline__ void prefetch_l2(const Chain &c, const Span &s, uint32_t off,
+                                            uint32_t sink) {
   const uint32_t o = at<REV>(s, off);
   if constexpr (SO)
     dma16_same2(rsrc(c.k + s.off, s.bytes), rsrc(c.v + s.off, s.bytes), o, sink);
@@ -418,7 +485,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 #pragma unroll
   for (int m = 0; m < NVG; ++m)
     voff[m] = lane_base<REV>(16 * (VG0 + m) + lane / 4,
-                             16u * ((lane % 4) ^ vswf(16 * (VG0 + m) + lane / 4)), rowbytes);
+                             16u * ((lane % 4) ^ vswf(16 * (VG0 + m) + lane / 4)), rowbytes) -
+              (REV ? 0u : 1024u * m);  // forward: copy m adds m KiB back (rows >= 16 m)
   const uint32_t ooff = lane_base<REV>(jrow, 8u * g, rowbytes);
   const char *vslice = c.v + 2 * c.c0;
   // This wave's share of the decayed V copy: lane bytes 16 (lane % 4) .. +15 of V rows
@@ -443,18 +511,25 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
   for (int ct = 0; ct < 2; ++ct) vpat[ct] = (uint32_t)vswz(trow, 16 * ct + tcol);
   const uint32_t dpat = (uint32_t)((16 * VG0 + lane / 4) * C::VROWB + 16 * (lane % 4));
 
-  auto issue = [&](int blk, uint32_t st_off) {
+  // Blocks whose DMA is issued next (wi) and whose outputs are stored next (ws).
+  Walk wi = walk_from<REV>(c, 0), ws = walk_from<REV>(c, 0);
+  auto issue = [&](uint32_t st_off) {
     const uint32_t st = smem_lds + st_off;
-    const Span sp = span<REV>(c, blk);
+    const Span sp = span_at<REV>(c, wi);
+    advance<REV>(c, wi);
     if constexpr (!SO && R < 3)
       dma_rows<D, REV>(c.q, sp, qoff[0], st + C::Q_OFF + 16 * R * C::ROWB);
     if constexpr (!SO && R == 1) dma_rows<D, REV>(c.q, sp, qoff[1], st + C::Q_OFF + 48 * C::ROWB);
     const uint32_t vl = st + C::V_OFF + 16 * VG0 * C::VROWB;  // 1 KiB per 16-row group
-    if constexpr (NVG == 2)
-      dma16x2(rsrc(vslice + sp.off, sp.bytes), at<REV>(sp, voff[0]), at<REV>(sp, voff[1]), vl,
-              vl + 1024);
-    else if constexpr (NVG == 1)
+    if constexpr (NVG == 2) {
+      if constexpr (REV)
+        dma16x2(rsrc(vslice + sp.off, sp.bytes), at<REV>(sp, voff[0]), at<REV>(sp, voff[1]), vl,
+                vl + 1024);
+      else
+        dma_kib2(rsrc(vslice + sp.off, sp.bytes), voff[0], voff[1], vl);
+    } else if constexpr (NVG == 1) {
       dma16(rsrc(vslice + sp.off, sp.bytes), at<REV>(sp, voff[0]), vl);
+    }
   };
   // Decayed copy of this wave's V rows of block blk (landed in the stage at st_off) into the same
   // stage.  All reads are issued before any write, so the LDS round trips overlap.
@@ -476,14 +551,14 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
   static_assert(NST == 3, "stage rotation and wait counts are written for three stages");
   // Stage offsets of blocks i (cur), i + 1 (nxt) and i + 2 (prv: the stage read in step i - 1).
   uint32_t s_cur = 0, s_nxt = C::STAGE, s_prv = 2 * C::STAGE;
-  issue(0, 0);
-  issue(1, C::STAGE);
+  issue(0);
+  issue(C::STAGE);
   if constexpr (DMA > 0) wait_vm<(NST - 2) * DMA>();  // own block-0 rows landed
   decay_v(0, 0);
   lds_barrier();  // block 0 and its decayed V visible to all waves
 
   for (int i = 0; i < c.nb; ++i) {
-    issue(i + NST - 1, s_prv);  // refills the stage read in step i-1
+    issue(s_prv);  // block i + 2, into the stage read in step i - 1
     if constexpr (!SO) {
       uint32_t kb[C::KSTEPS], vb[2];
 #pragma unroll
@@ -560,7 +635,7 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 
       // Store: lane holds O[jrow][c0 + 16ct + 4g + 0..3]; rows past the end are dropped.
       {
-        const Span sp = span<REV>(c, i);
+        const Span sp = span_at<REV>(c, ws);
         const auto ro = rsrc(c.out + sp.off, sp.bytes);
         const uint32_t off = at<REV>(sp, ooff);
 #pragma unroll
@@ -570,13 +645,12 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       }
     }  // !SO
 
+    advance<REV>(c, ws);
     // Own rows of block i+1 landed: its DMA was issued in step i-1 (or the prologue); since
-    // then this wave issued that step's stores, this step's DMA and stores.
-    static_assert(NST == 3, "wait counts are written for three stages");
-    if constexpr (DMA > 0) {
-      if (i == 0) wait_vm<DMA + STORES>();
-      else wait_vm<DMA + 2 * STORES>();
-    }
+    // then this wave issued that step's stores (none in the prologue), this step's DMA and
+    // stores.  Counting one step's stores only waits for step i-1's stores too, which were
+    // issued a step ago.
+    if constexpr (DMA > 0) wait_vm<DMA + STORES>();
     decay_v(i + 1, s_nxt);
     lds_barrier();
     const uint32_t so = s_cur;
@@ -655,26 +729,35 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   uint32_t koff[C::QK_DMA];
   rows_offsets<D, REV>(R, lane, c.rowbytes, koff);
   const uint32_t pfoff = prefetch_offset<D, REV>(c.slice, lane, c.rowbytes);
-  auto issue = [&](int blk, uint32_t st_off) {
+  // Blocks whose K rows (wk) and L2 prefetch (wp) are issued next.
+  Walk wk = walk_from<REV>(c, 0), wp = walk_from<REV>(c, PF_AHEAD);
+  auto issue = [&](uint32_t st_off) {
     const uint32_t st = smem_lds + st_off;
-    dma_rows<D, REV>(c.k, span<REV>(c, blk), koff, st + C::K_OFF + 16 * R * C::ROWB);
+    dma_rows<D, REV>(c.k, span_at<REV>(c, wk), koff, st + C::K_OFF + 16 * R * C::ROWB);
+    advance<REV>(c, wk);
     // after the DMA, so that waiting for this DMA never waits for a prefetch (counters are
     // in order)
-    if constexpr (PF) prefetch_l2<SO, REV>(c, blk + PF_AHEAD, pfoff, smem_lds + C::PF_OFF);
+    if constexpr (PF) {
+      prefetch_l2<SO, REV>(c, span_at<REV>(c, wp), pfoff, smem_lds + C::PF_OFF);
+      advance<REV>(c, wp);
+    }
   };
   if constexpr (PF) {
     // Blocks NST-1 .. PF_AHEAD-1 are not covered by the prefetches of the first issues.
     for (int blk = NST - 1; blk < PF_AHEAD; ++blk)
-      prefetch_l2<SO, REV>(c, blk, pfoff, smem_lds + C::PF_OFF);
+      prefetch_l2<SO, REV>(c, span_at<REV>(c, walk_from<REV>(c, blk)), pfoff,
+                           smem_lds + C::PF_OFF);
   }
   static_assert(NST == 3, "stage rotation is written for three stages");
   uint32_t s_cur = 0, s_nxt = C::STAGE, s_prv = 2 * C::STAGE;
-  issue(0, 0);
-  issue(1, C::STAGE);
+  issue(0);
+  issue(C::STAGE);
   wait_vm_barrier<WAIT>();
 
   for (int i = 0; i < c.nb; ++i) {
-    issue(i + NST - 1, s_prv);
+    // A wave with a band issues its copies once its MFMAs are queued (they overlap them);
+    // the copies of block i + 2 only need to land by the end of step i + 1.
+    if constexpr (RT == 0) issue(s_prv);
     if constexpr (RT > 0) {
       uint32_t kb[RT], vb[2];
 #pragma unroll
@@ -710,6 +793,7 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
           for (int ct = 0; ct < 2; ++ct) kv[rt][ct] = mfma(kop, vop[ct], kv[rt][ct]);
         }
       }
+      issue(s_prv);  // block i + 2
       write_kvx(s_nxt);
     }
     // Block i+1's K rows landed: since their DMA this wave issued only the later issues.
@@ -783,6 +867,10 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   c.nb = (int)((c.n + BLK - 1) / BLK);
   c.b_last = c.nb > 0 ? (int)(c.n - (int64_t)(c.nb - 1) * BLK) : BLK;
   c.rowbytes = (uint32_t)H * D * 2;
+  c.full_bytes = (uint32_t)BLK * c.rowbytes;
+  c.last_bytes = (uint32_t)c.b_last * c.rowbytes;
+  c.full_last = (uint32_t)(BLK - 1) * c.rowbytes;
+  c.last_last = (uint32_t)(c.b_last - 1) * c.rowbytes;
   c.c0 = slice * CV;
   c.slice = slice;
   c.out = (char *)(out + first + c.c0);
