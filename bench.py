@@ -167,6 +167,7 @@ def main():
         del q, k, v, out
         result["few_chain_prefill"] = few_chain_prefill(dev)
         result["backward"] = backward_leg(wl, dev)
+        result["few_chain_backward"] = few_chain_backward(dev)
         result["decode_tokens"] = decode_tokens_leg(dev)
     if not args.no_cpu_baseline:
         q, k, v = wl.inputs(device=dev)
@@ -270,6 +271,27 @@ def few_chain_prefill(dev, iters=20, warmup=3):
                     "split_tokens_per_s": T / (split / 1e3)})
         del q, k, v, o
     return res
+
+
+def few_chain_backward(dev, iters=10, warmup=2):
+    """Backward of 65,536 tokens x 8 heads (one device's share of the 64-head layer under
+    8-way head sharding): the three gradient scans plain and sequence-split."""
+    import torch
+
+    import long_context_attention_attn_amd as la
+    from long_context_attention_attn_amd import _lib, synth
+
+    T, Hc = 65536, 8
+    q, k, v = synth.qkv(T, Hc, D, torch.bfloat16, seed=0, device=dev)
+    do, _, _ = synth.qkv(T, Hc, D, torch.bfloat16, seed=50, device=dev)
+    dec = synth.decay_geometric(Hc, 0.9, 0.9999).to(dev)
+    seg = _lib.prefill_split_blocks(T, 1, Hc, D)
+    plain = time_ms(lambda: la.backward(q, k, v, dec, do), iters, warmup)
+    split = time_ms(lambda: la.backward(q, k, v, dec, do, split=seg or None), iters, warmup)
+    nbytes = backward_bytes(T, Hc, D)
+    return {"tokens": T, "heads": Hc, "seg_blocks": seg, "plain_ms": plain, "split_ms": split,
+            "speedup": plain / split, "split_algorithmic_GBps": nbytes / (split / 1e3) / 1e9,
+            "split_tokens_per_s": T / (split / 1e3)}
 
 
 def measured_traffic():

@@ -121,9 +121,9 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
                            la_dtype dtype, int32_t seg_blocks, void *workspace,
                            size_t workspace_bytes, void *stream);
 
-/* Workspace bytes la_prefill_split needs for these sizes (0 for invalid sizes).  The bound
- * holds for any valid cu_seqlens: (ceil(T / (64 seg_blocks)) + S - 1) states of H*D*D floats
- * plus the segment table. */
+/* Workspace bytes la_prefill_split and la_backward_split need for these sizes (0 for invalid
+ * sizes).  The bound holds for any valid cu_seqlens: (ceil(T / (64 seg_blocks)) + S - 1) states
+ * of H*D*D floats plus the segment table. */
 size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t D,
                                        int32_t seg_blocks);
 
@@ -163,6 +163,30 @@ la_status la_backward(const void *q, const void *k, const void *v, const float *
                       const float *d_final_state, void *dq, void *dk, void *dv,
                       float *d_initial_state, int64_t T, int32_t S, int32_t H, int32_t D,
                       la_dtype dtype, void *stream);
+
+/*
+ * la_backward with every sequence cut into segments of seg_blocks blocks that are scanned in
+ * parallel, for batches with few (sequence, head) pairs (the construction of la_prefill_split,
+ * applied to the three gradient scans).  dq: segment states of the forward scan, combined from
+ * S0^T, then every segment from its incoming state.  dk and dv: their reversed-time states are
+ * transposes of each other, so one reversed state-only pass over the segments serves both; the
+ * combine walks each sequence's segments from the last to the first starting from dSn, and its
+ * result times lambda is dS0; then every segment of dv and of dk from its incoming state (the
+ * last segment of a sequence, met first, from dSn as the unsplit scans use it).  Eight launches
+ * on `stream`.  The result differs from la_backward only in rounding order.
+ *
+ *   seg_blocks, workspace, workspace_bytes: as la_prefill_split; the workspace size is
+ *                 la_prefill_split_workspace_size(T, S, H, D, seg_blocks) and must not overlap
+ *                 any other argument
+ *   T < 2^31; all other arguments as la_backward.
+ * Errors: as la_backward, plus those of la_prefill_split's workspace and segment arguments.
+ */
+la_status la_backward_split(const void *q, const void *k, const void *v, const float *decay,
+                            const int32_t *cu_seqlens, const float *initial_state,
+                            const void *d_out, const float *d_final_state, void *dq, void *dk,
+                            void *dv, float *d_initial_state, int64_t T, int32_t S, int32_t H,
+                            int32_t D, la_dtype dtype, int32_t seg_blocks, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent decode step for Bt independent sequences (one new token each):

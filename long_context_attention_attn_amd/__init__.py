@@ -102,13 +102,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
         _check_act("final_state", final_state, torch.float32, device)
         if final_state.shape != (S, H, D, D):
             raise ValueError("final_state must be [S, H, D, D]")
-    seg_blocks = 0
-    if split == "auto":
-        seg_blocks = _lib.prefill_split_blocks(T, S, H, D)
-    elif split is not None:
-        if isinstance(split, bool) or not isinstance(split, int) or split < 1:
-            raise ValueError("split must be None, 'auto' or an int >= 1")
-        seg_blocks = split
+    seg_blocks = _seg_blocks(split, T, S, H, D)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
             0 if cu_seqlens is None else cu_seqlens.data_ptr(),
             0 if initial_state is None else initial_state.data_ptr(),
@@ -125,15 +119,27 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
     return out, final_state
 
 
+def _seg_blocks(split, T, S, H, D) -> int:
+    """Segment length (in 64-token blocks) for ``split``; 0 = no sequence split."""
+    if split == "auto":
+        return _lib.prefill_split_blocks(T, S, H, D)
+    if split is None:
+        return 0
+    if isinstance(split, bool) or not isinstance(split, int) or split < 1:
+        raise ValueError("split must be None, 'auto' or an int >= 1")
+    return split
+
+
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,
              d_out: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None, *,
              initial_state: Optional[torch.Tensor] = None,
              d_final_state: Optional[torch.Tensor] = None,
-             want_d_initial_state: bool = True):
+             want_d_initial_state: bool = True, split: Union[None, str, int] = None):
     """Gradients of the prefill: (dq, dk, dv [T, H, D], d_initial_state [S, H, D, D] or None).
 
     q, k, v, decay, cu_seqlens, initial_state: the prefill's inputs; d_out [T, H, D] (same dtype
-    as q) is dL/dout, d_final_state [S, H, D, D] fp32 (or None = 0) is dL/dfinal_state."""
+    as q) is dL/dout, d_final_state [S, H, D, D] fp32 (or None = 0) is dL/dfinal_state.
+    split: as for prefill (the sequence-split form of the three gradient scans)."""
     device = q.device
     if q.dim() != 3:
         raise ValueError("q must be [T, H, D]")
@@ -163,12 +169,19 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Ten
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     d_init = (torch.empty((S, H, D, D), dtype=torch.float32, device=device)
               if want_d_initial_state else None)
-    _lib.backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
-                  0 if cu_seqlens is None else cu_seqlens.data_ptr(),
-                  0 if initial_state is None else initial_state.data_ptr(), d_out.data_ptr(),
-                  0 if d_final_state is None else d_final_state.data_ptr(), dq.data_ptr(),
-                  dk.data_ptr(), dv.data_ptr(), 0 if d_init is None else d_init.data_ptr(),
-                  T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
+            0 if cu_seqlens is None else cu_seqlens.data_ptr(),
+            0 if initial_state is None else initial_state.data_ptr(), d_out.data_ptr(),
+            0 if d_final_state is None else d_final_state.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), 0 if d_init is None else d_init.data_ptr())
+    seg_blocks = _seg_blocks(split, T, S, H, D)
+    if seg_blocks > 0:
+        nbytes = _lib.prefill_split_workspace_size(T, S, H, D, seg_blocks)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _lib.backward_split(*ptrs, T, S, H, D, _DTYPES[dtype], seg_blocks, ws.data_ptr(), nbytes,
+                            _stream_ptr(device))
+    else:
+        _lib.backward(*ptrs, T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
     return dq, dk, dv, d_init
 
 
@@ -179,6 +192,7 @@ class _LightningAttention(torch.autograd.Function):
     def forward(ctx, q, k, v, decay, cu_seqlens, initial_state, split):
         out, fs = prefill(q, k, v, decay, cu_seqlens, initial_state=initial_state, split=split)
         ctx.save_for_backward(q, k, v, decay, cu_seqlens, initial_state)
+        ctx.split = split
         return out, fs
 
     @staticmethod
@@ -187,7 +201,8 @@ class _LightningAttention(torch.autograd.Function):
         dq, dk, dv, d_init = backward(
             q, k, v, decay, d_out.contiguous(), cu_seqlens, initial_state=initial_state,
             d_final_state=None if d_fs is None else d_fs.contiguous(),
-            want_d_initial_state=initial_state is not None and ctx.needs_input_grad[5])
+            want_d_initial_state=initial_state is not None and ctx.needs_input_grad[5],
+            split=ctx.split)
         return dq, dk, dv, None, None, d_init, None
 
 
@@ -196,7 +211,8 @@ def lightning_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay
                         initial_state: Optional[torch.Tensor] = None,
                         split: Union[None, str, int] = None):
     """Differentiable prefill: (out, final_state); backward runs the library's gradient
-    scans.  decay and cu_seqlens get no gradient."""
+    scans (sequence-split too when ``split`` is given).  decay and cu_seqlens get no
+    gradient."""
     return _LightningAttention.apply(q, k, v, decay, cu_seqlens, initial_state, split)
 
 

@@ -22,6 +22,7 @@ LA_F32, LA_BF16 = 0, 1
 # Every symbol declared in include/lightning_attn.h.
 EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_split",
            "la_prefill_split_workspace_size", "la_prefill_split_blocks", "la_backward",
+           "la_backward_split",
            "la_decode_step", "la_decode_tokens",
            "la_status_str", "la_last_error")
 
@@ -75,6 +76,10 @@ def load():
         lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32,
                                     i32, i32, ctypes.c_int, vp]
         lib.la_backward.restype = ctypes.c_int
+        lib.la_backward_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                          i32, i32, i32, ctypes.c_int, i32, vp, ctypes.c_size_t,
+                                          vp]
+        lib.la_backward_split.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
@@ -129,6 +134,15 @@ def backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state, dq
     _raise(load().la_backward(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens), _p(initial_state),
                               _p(d_out), _p(d_final_state), _p(dq), _p(dk), _p(dv),
                               _p(d_initial_state), T, S, H, D, dtype, _p(stream)))
+
+
+def backward_split(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state, dq, dk, dv,
+                   d_initial_state, T, S, H, D, dtype, seg_blocks, workspace, workspace_bytes,
+                   stream):
+    _raise(load().la_backward_split(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens),
+                                    _p(initial_state), _p(d_out), _p(d_final_state), _p(dq),
+                                    _p(dk), _p(dv), _p(d_initial_state), T, S, H, D, dtype,
+                                    seg_blocks, _p(workspace), workspace_bytes, _p(stream)))
 
 
 def decode_step(q, k, v, decay, state, out, Bt, H, D, dtype, stream):

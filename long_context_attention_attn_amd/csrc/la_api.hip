@@ -107,7 +107,7 @@ int64_t split_capacity(int64_t T, int32_t S, int64_t seg_len) {
 
 struct SplitLayout {
   int64_t cap;
-  size_t states, seg_cu, seq_seg0, bytes;  // byte offsets and total size
+  size_t states, seg_cu, seq_seg0, seg_rfirst, bytes;  // byte offsets and total size
 };
 
 SplitLayout split_layout(int64_t T, int32_t S, int32_t H, int32_t D, int32_t seg_blocks) {
@@ -116,7 +116,8 @@ SplitLayout split_layout(int64_t T, int32_t S, int32_t H, int32_t D, int32_t seg
   l.states = 0;
   l.seg_cu = align256((size_t)l.cap * H * D * D * sizeof(float));
   l.seq_seg0 = l.seg_cu + align256((size_t)(l.cap + 1) * sizeof(int32_t));
-  l.bytes = l.seq_seg0 + align256((size_t)(S + 1) * sizeof(int32_t));
+  l.seg_rfirst = l.seq_seg0 + align256((size_t)(S + 1) * sizeof(int32_t));
+  l.bytes = l.seg_rfirst + align256((size_t)l.cap * sizeof(int32_t));
   return l;
 }
 
@@ -254,7 +255,7 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   auto prefill = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
 
   hipError_t e = la_launch_seg_table(cu_seqlens, T, S, (int64_t)seg_blocks * 64, cap, seg_cu,
-                                     seq_seg0, s);
+                                     seq_seg0, nullptr, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "segment table launch: %s", hipGetErrorString(e));
   // Segment states from zero: only k and v are read.
   LaPrefillArgs a{};
@@ -270,7 +271,8 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   a.state_only = true;
   e = prefill(a, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "segment state launch: %s", hipGetErrorString(e));
-  e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, final_state, s);
+  e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, final_state,
+                        false, false, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   // Every segment from its incoming state.
   a.q = q;
@@ -283,12 +285,15 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   return LA_OK;
 }
 
-la_status la_backward(const void *q, const void *k, const void *v, const float *decay,
-                      const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
-                      const float *d_final_state, void *dq, void *dk, void *dv,
-                      float *d_initial_state, int64_t T, int32_t S, int32_t H, int32_t D,
-                      la_dtype dtype, void *stream) {
-  g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the backward entry points (no device access).
+la_status check_backward(const void *q, const void *k, const void *v, const float *decay,
+                         const int32_t *cu_seqlens, const float *initial_state,
+                         const void *d_out, const float *d_final_state, const void *dq,
+                         const void *dk, const void *dv, const float *d_initial_state,
+                         int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype) {
   la_status st = check_common(q, k, v, decay, d_out, T, H, D, dtype);
   if (st != LA_OK) return st;
   if (T > 0) {
@@ -315,6 +320,21 @@ la_status la_backward(const void *q, const void *k, const void *v, const float *
         overlaps(d_initial_state, stb, d_final_state, stb))
       return fail(LA_ERR_INVALID_ARG, "d_initial_state overlaps a state input");
   }
+  return LA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+la_status la_backward(const void *q, const void *k, const void *v, const float *decay,
+                      const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
+                      const float *d_final_state, void *dq, void *dk, void *dv,
+                      float *d_initial_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                      la_dtype dtype, void *stream) {
+  g_err[0] = '\0';
+  la_status st = check_backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state,
+                                dq, dk, dv, d_initial_state, T, S, H, D, dtype);
+  if (st != LA_OK) return st;
   if (T == 0 && d_initial_state == nullptr) return LA_OK;
   st = check_device();
   if (st != LA_OK) return st;
@@ -366,6 +386,128 @@ la_status la_backward(const void *q, const void *k, const void *v, const float *
   a.final_state = d_initial_state;
   e = scan(a, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "dv launch: %s", hipGetErrorString(e));
+  return LA_OK;
+}
+
+la_status la_backward_split(const void *q, const void *k, const void *v, const float *decay,
+                            const int32_t *cu_seqlens, const float *initial_state,
+                            const void *d_out, const float *d_final_state, void *dq, void *dk,
+                            void *dv, float *d_initial_state, int64_t T, int32_t S, int32_t H,
+                            int32_t D, la_dtype dtype, int32_t seg_blocks, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  g_err[0] = '\0';
+  la_status st = check_backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state,
+                                dq, dk, dv, d_initial_state, T, S, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (seg_blocks < 1) return fail(LA_ERR_INVALID_ARG, "seg_blocks = %d < 1", seg_blocks);
+  if (T > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "split backward needs T < 2^31");
+  if (T == 0)  // no segments
+    return la_backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state, dq, dk,
+                       dv, d_initial_state, T, S, H, D, dtype, stream);
+  const SplitLayout lay = split_layout(T, S, H, D, seg_blocks);
+  if (lay.cap * H * (D / 32) > 0x7fffffffLL || (long long)S * H * (D * D / 256) > 0x7fffffffLL)
+    return fail(LA_ERR_INVALID_ARG, "too many segments");
+  if (workspace == nullptr) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(LA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay.bytes)
+    return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                lay.bytes);
+  {
+    const size_t act = (size_t)T * H * D * elem_bytes(dtype);
+    const size_t stb = (size_t)S * H * D * D * sizeof(float);
+    const void *acts[7] = {q, k, v, d_out, dq, dk, dv};
+    for (const void *x : acts)
+      if (overlaps(workspace, lay.bytes, x, act))
+        return fail(LA_ERR_INVALID_ARG, "workspace overlaps an argument buffer");
+    if (overlaps(workspace, lay.bytes, initial_state, stb) ||
+        overlaps(workspace, lay.bytes, d_final_state, stb) ||
+        overlaps(workspace, lay.bytes, d_initial_state, stb) ||
+        overlaps(workspace, lay.bytes, decay, (size_t)H * sizeof(float)) ||
+        overlaps(workspace, lay.bytes, cu_seqlens, (size_t)(S + 1) * sizeof(int32_t)))
+      return fail(LA_ERR_INVALID_ARG, "workspace overlaps an argument buffer");
+  }
+  st = check_device();
+  if (st != LA_OK) return st;
+
+  char *ws = static_cast<char *>(workspace);
+  float *states = reinterpret_cast<float *>(ws + lay.states);
+  int32_t *seg_cu = reinterpret_cast<int32_t *>(ws + lay.seg_cu);
+  int32_t *seq_seg0 = reinterpret_cast<int32_t *>(ws + lay.seq_seg0);
+  int32_t *seg_rfirst = reinterpret_cast<int32_t *>(ws + lay.seg_rfirst);
+  const int32_t cap = (int32_t)lay.cap;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto scan = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
+
+  hipError_t e = la_launch_seg_table(cu_seqlens, T, S, (int64_t)seg_blocks * 64, cap, seg_cu,
+                                     seq_seg0, seg_rfirst, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment table launch: %s", hipGetErrorString(e));
+
+  // dq: the forward scan (query, key, value) = (do, v, k) from S0^T, split like the prefill.
+  LaPrefillArgs a{};
+  a.k = v;
+  a.v = k;
+  a.decay = decay;
+  a.cu_seqlens = seg_cu;
+  a.final_state = states;
+  a.T = T;
+  a.S = cap;
+  a.H = H;
+  a.D = D;
+  a.state_only = true;
+  e = scan(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dq segment states: %s", hipGetErrorString(e));
+  e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, nullptr, true,
+                        false, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dq combine: %s", hipGetErrorString(e));
+  a.q = d_out;
+  a.out = dq;
+  a.initial_state = states;
+  a.final_state = nullptr;
+  a.state_only = false;
+  e = scan(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dq segments: %s", hipGetErrorString(e));
+
+  // dv and dk: reversed scans (k, q, do) and (v, do, q) whose states are transposes of each
+  // other, so one set of segment states serves both: states of (key, value) = (q, do) from
+  // zero, combined from dSn in reversed segment order (dSn inclusive), which also gives dS0.
+  LaPrefillArgs b{};
+  b.k = q;
+  b.v = d_out;
+  b.decay = decay;
+  b.cu_seqlens = seg_cu;
+  b.final_state = states;
+  b.T = T;
+  b.S = cap;
+  b.H = H;
+  b.D = D;
+  b.reverse = true;
+  b.state_only = true;
+  e = scan(b, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dv/dk segment states: %s", hipGetErrorString(e));
+  e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, d_final_state, states, d_initial_state,
+                        false, true, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dv/dk combine: %s", hipGetErrorString(e));
+  // Each segment from its incoming state; the last segment of a sequence (met first by the
+  // reversed scan) starts from dSn, which counts as inclusive.
+  b.q = k;
+  b.k = q;
+  b.v = d_out;
+  b.out = dv;
+  b.initial_state = states;
+  b.final_state = nullptr;
+  b.state_only = false;
+  b.init_inclusive = true;
+  b.seq_incl = seg_rfirst;
+  e = scan(b, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dv segments: %s", hipGetErrorString(e));
+  b.q = v;
+  b.k = d_out;
+  b.v = q;
+  b.out = dk;
+  b.init_transposed = true;
+  e = scan(b, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "dk segments: %s", hipGetErrorString(e));
   return LA_OK;
 }
 

@@ -21,6 +21,8 @@ struct LaPrefillArgs {
                          // and the final state multiplied by lambda when the sequence is non-empty
   bool init_transposed;  // read initial_state[s][h][b][a] as element [a][b]
   bool state_only;       // compute only final_state (q and out unused, may be NULL)
+  const int32_t *seq_incl = nullptr;  // [S] or nullptr: with init_inclusive, only sequences s
+                                      // with seq_incl[s] != 0 count their initial state inclusive
 };
 
 struct LaDecodeArgs {
@@ -43,7 +45,10 @@ hipError_t la_launch_decode_multi_f32(const LaDecodeArgs &a, int32_t m, hipStrea
 // Sequence split (split.hip).
 hipError_t la_launch_seg_table(const int32_t *cu, int64_t T, int32_t S, int64_t seg_len,
                                int32_t cap, int32_t *seg_cu, int32_t *seq_seg0,
-                               hipStream_t stream);
+                               int32_t *seg_rfirst, hipStream_t stream);
+// s0_transposed: read s0[s][h][b][a] as element [a][b].  reverse_inclusive: walk each sequence's
+// segments from last to first (a reversed scan), the first one counting s0 as inclusive.
 hipError_t la_launch_combine(const float *decay, const int32_t *seg_cu, const int32_t *seq_seg0,
                              int32_t S, int32_t H, int32_t D, const float *s0, float *st,
-                             float *fs, hipStream_t stream);
+                             float *fs, bool s0_transposed, bool reverse_inclusive,
+                             hipStream_t stream);

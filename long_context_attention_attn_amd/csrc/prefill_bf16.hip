@@ -818,14 +818,15 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   }
 }
 
-// flags: bit 1 inclusive initial state, bit 2 transposed initial state.  SO: compute only the
+// flags: bit 1 inclusive initial state (only for sequences s with incl_v[s] != 0 when incl_v is
+// given), bit 2 transposed initial state.  SO: compute only the
 // final state (q and out are not touched).  REV: reversed (anti-causal) scan.
 template <int D, bool SO, bool REV>
 __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, __bf16 *__restrict__ out, float *__restrict__ fs, int64_t T,
-    int S, int H, int flags) {
+    int S, int H, int flags, const int32_t *__restrict__ incl_v) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -874,7 +875,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   c.c0 = slice * CV;
   c.slice = slice;
   c.out = (char *)(out + first + c.c0);
-  c.incl = flags & 2;
+  c.incl = (flags & 2) && (incl_v == nullptr || incl_v[seq] != 0);
   c.s0t = flags & 4;
 
   const int tid = threadIdx.x;
@@ -913,14 +914,15 @@ hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_bf16_kernel<D, SO, REV>), dim3((unsigned)grid), dim3(NTHR), 0, stream,
                      (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, a.decay,
                      a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state, a.T, a.S,
-                     a.H, flags);
+                     a.H, flags, a.seq_incl);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t la_launch_prefill_bf16(const LaPrefillArgs &a, hipStream_t stream) {
-  if (a.state_only && a.reverse) return hipErrorInvalidValue;  // not instantiated (unused)
+  if (a.state_only && a.reverse)
+    return a.D == 128 ? launch<128, true, true>(a, stream) : launch<64, true, true>(a, stream);
   if (a.state_only)
     return a.D == 128 ? launch<128, true, false>(a, stream) : launch<64, true, false>(a, stream);
   if (a.reverse)

@@ -23,8 +23,8 @@ __global__ __launch_bounds__(NTHR) void prefill_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ fs, int64_t T,
-    int H, int flags) {
-  const bool rev = flags & 1, incl = flags & 2, s0t = flags & 4, so = flags & 8;
+    int H, int flags, const int32_t *__restrict__ incl_v) {
+  const bool rev = flags & 1, s0t = flags & 4, so = flags & 8;
   constexpr int NS = D / CV;
   __shared__ float Qs[BLK][D + 1];
   __shared__ float Ks[BLK][D + 1];
@@ -35,6 +35,7 @@ __global__ __launch_bounds__(NTHR) void prefill_f32_kernel(
 
   const int chain = blockIdx.x / NS, slice = blockIdx.x % NS;
   const int seq = chain / H, h = chain % H;
+  const bool incl = (flags & 2) && (incl_v == nullptr || incl_v[seq] != 0);
   const int64_t tok0 = cu ? (int64_t)cu[seq] : 0;
   const int64_t tok1 = cu ? (int64_t)cu[seq + 1] : T;
   const int64_t n = tok1 > tok0 ? tok1 - tok0 : 0;
@@ -118,7 +119,8 @@ hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
                      (const float *)a.q, (const float *)a.k, (const float *)a.v, a.decay,
                      a.cu_seqlens, a.initial_state, (float *)a.out, a.final_state, a.T, a.H,
                      (a.reverse ? 1 : 0) | (a.init_inclusive ? 2 : 0) |
-                         (a.init_transposed ? 4 : 0) | (a.state_only ? 8 : 0));
+                         (a.init_transposed ? 4 : 0) | (a.state_only ? 8 : 0),
+                     a.seq_incl);
   return hipGetLastError();
 }
 

@@ -137,7 +137,7 @@ def test_split_workspace_size(lib):
     def expect(T, S, H, D, nb):
         a = lambda x: (x + 255) // 256 * 256
         cap = -(-T // (64 * nb)) + S - 1 if T > 0 else 0
-        return a(cap * H * D * D * 4) + a((cap + 1) * 4) + a((S + 1) * 4)
+        return a(cap * H * D * D * 4) + a((cap + 1) * 4) + a((S + 1) * 4) + a(cap * 4)
 
     for args in [(8192, 1, 8, 128, 16), (1000, 3, 2, 64, 1), (1, 1, 1, 128, 7), (0, 2, 4, 64, 2),
                  (272568, 16, 64, 128, 64)]:
@@ -242,3 +242,28 @@ def test_split_workspace_overlap_rejected(lib, ws):
     # a workspace that overlaps q (at P), out (at P2) or the final states (at 0x700000)
     assert _split(lib, ws=ctypes.c_void_p(ws), fs=ctypes.c_void_p(0x700000)) == 1
     assert b"overlap" in lib.la_last_error()
+
+
+def _backward_split(lib, seg_blocks=4, ws=ctypes.c_void_p(0x800000), ws_bytes=1 << 30, T=1000,
+                    dq=G1, q=P, D=128):
+    return lib.la_backward_split(q, P, P, P, None, None, P2, None, dq, G2, G3, None, T, 1, 2, D,
+                                 1, seg_blocks, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(seg_blocks=0), 1), (dict(ws=None), 1), (dict(ws=ctypes.c_void_p(0x800010)), 1),
+    (dict(ws_bytes=4096), 1), (dict(T=1 << 31), 1), (dict(dq=None), 1), (dict(D=80), 2),
+    # workspace over dq (at 0x400000) or over q (at 0x100000)
+    (dict(ws=ctypes.c_void_p(0x400000)), 1), (dict(ws=ctypes.c_void_p(0x100000)), 1),
+])
+def test_backward_split_validation(lib, kwargs, status):
+    assert _backward_split(lib, **kwargs) == status
+    assert lib.la_last_error() != b""
+
+
+def test_backward_split_without_device(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _backward_split(lib) == 3

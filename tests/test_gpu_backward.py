@@ -131,3 +131,81 @@ def test_autograd_function(dtype):
     want = oracle.backward(q, k, v, decay, W, cu, init_state=init, d_final=W2)
     got = (qg.grad, kg.grad, vg.grad, sg.grad)
     _compare(got, want, cu, TOL[dtype], "autograd")
+
+
+def _gpu_backward_split(q, k, v, decay, do, cu, init, dfs, seg_blocks):
+    d = dev()
+    g = la.backward(q.to(d), k.to(d), v.to(d), decay.to(d), do.to(d),
+                    None if cu is None else cu.to(d),
+                    initial_state=None if init is None else init.to(d),
+                    d_final_state=None if dfs is None else dfs.to(d), split=seg_blocks)
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("with_states", [False, True], ids=["no_states", "states"])
+@pytest.mark.parametrize("seg_blocks", [1, 2])
+def test_backward_split_ragged_varlen(dtype, D, with_states, seg_blocks):
+    """The sequence-split backward on the ragged batch (segments of 64 or 128 tokens cut the
+    65-, 130- and 200-token sequences; the last segment of the 65-token one has a single token,
+    where the reversed scans' first segment decays dSn by lambda^0; lambda = 0, 0.95, 1): every
+    row against O6, and dS0 of the empty sequence = dSn."""
+    banner("backward split ragged dtype=%s D=%d states=%s seg_blocks=%d"
+           % (dtype, D, with_states, seg_blocks))
+    H = 3
+    cu = synth.cu_from_lengths(RAGGED)
+    T = int(cu[-1])
+    q, k, v = synth.qkv(T, H, D, dtype, seed=3)
+    do, _, _ = synth.qkv(T, H, D, dtype, seed=30)
+    decay = torch.tensor([0.0, 0.95, 1.0], dtype=torch.float32)
+    init = synth.random_state(len(RAGGED), H, D, seed=4, scale=0.1) if with_states else None
+    dfs = synth.random_state(len(RAGGED), H, D, seed=31, scale=0.1) if with_states else None
+    got = _gpu_backward_split(q, k, v, decay, do, cu, init, dfs, seg_blocks)
+    want = oracle.backward(q, k, v, decay, do, cu, init_state=init, d_final=dfs)
+    _compare(got, want, cu, TOL[dtype], "split ragged")
+    if with_states:
+        assert torch.equal(got[3][4].cpu(), dfs[4])
+    else:
+        assert torch.count_nonzero(got[3][4]).item() == 0
+
+
+def test_backward_split_8k_recurrent():
+    """8 heads x 8,192 tokens, D=128, bf16, 16-block segments (8 per sequence), with an initial
+    state and a final-state gradient: all heads against O7, and against the unsplit backward."""
+    wl = synth.workloads()["prefill_8k"]
+    banner("backward split prefill_8k T=8192 H=8 D=128 bf16 seg_blocks=16")
+    q, k, v = wl.inputs()
+    do, _, _ = synth.qkv(wl.T, wl.H, wl.D, torch.bfloat16, seed=40)
+    decay = wl.decay()
+    init = synth.random_state(1, wl.H, wl.D, seed=41, scale=0.05)
+    dfs = synth.random_state(1, wl.H, wl.D, seed=42, scale=0.05)
+    got = _gpu_backward_split(q, k, v, decay, do, None, init, dfs, 16)
+    want = oracle.backward_recurrent(q, k, v, decay, do, init_state=init, d_final=dfs)
+    _compare(got, want, [0, wl.T], BF16_TOL, "split 8k")
+    plain = _gpu_backward(q, k, v, decay, do, None, init, dfs)
+    for name, a, b in zip(("dq", "dk", "dv"), got[:3], plain[:3]):
+        e = slice_errors(to_np(a), to_np(b).astype(np.float64), [0, wl.T])
+        assert float(e.max()) <= BF16_TOL, name
+    e = state_errors(to_np(got[3]), to_np(plain[3]).astype(np.float64))
+    assert float(e.max()) <= 1e-4
+
+
+def test_autograd_split_matches_plain():
+    """lightning_attention(split=2) gives the same gradients as split=None (fp32, 2 heads,
+    ragged lengths), within fp32 rounding."""
+    banner("autograd split vs plain")
+    d = dev()
+    cu = synth.cu_from_lengths([300, 5, 129]).to(d)
+    T = 434
+    grads = []
+    for split in (None, 2):
+        q, k, v = (x.to(d).requires_grad_(True) for x in synth.qkv(T, 2, 64, torch.float32, seed=7))
+        decay = torch.tensor([0.9, 0.99], device=d)
+        init = synth.random_state(3, 2, 64, seed=8, scale=0.1).to(d).requires_grad_(True)
+        out, fs = la.lightning_attention(q, k, v, decay, cu, initial_state=init, split=split)
+        (out.square().sum() + fs.square().sum()).backward()
+        grads.append([x.grad.detach().cpu().double() for x in (q, k, v, init)])
+    for a, b in zip(*grads):
+        assert float((a - b).norm() / b.norm()) <= 1e-4
