@@ -209,3 +209,24 @@ def test_autograd_split_matches_plain():
         grads.append([x.grad.detach().cpu().double() for x in (q, k, v, init)])
     for a, b in zip(*grads):
         assert float((a - b).norm() / b.norm()) <= 1e-4
+
+
+def test_backward_split_empty_and_deterministic():
+    """Split backward: a batch of empty sequences (no segments) leaves dS0 = dSn; two calls on
+    the same inputs give bitwise-equal gradients."""
+    banner("backward split empty batch and determinism")
+    d = dev()
+    H, D = 2, 128
+    dfs = synth.random_state(2, H, D, seed=70, scale=0.1)
+    z = torch.zeros((0, H, D), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 0, 0], dtype=torch.int32)
+    decay = torch.tensor([0.9, 0.5], dtype=torch.float32)
+    _, _, _, di = _gpu_backward_split(z, z, z, decay, z, cu, None, dfs, 4)
+    assert torch.equal(di.cpu(), dfs)
+    q, k, v = synth.qkv(3000, 4, 128, torch.bfloat16, seed=60)
+    do, _, _ = synth.qkv(3000, 4, 128, torch.bfloat16, seed=61)
+    dec = synth.decay_geometric(4, 0.9, 0.999)
+    a = _gpu_backward_split(q, k, v, dec, do, None, None, None, 4)
+    b = _gpu_backward_split(q, k, v, dec, do, None, None, None, 4)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -7,8 +7,8 @@
 * 1,048,576 tokens x 64 heads (int64 indexing: T*H*D > 2^31): heads {0, 21, 42, 63} against
   the recurrent form;
 * one decode step for 256 sequences x 64 heads of fp32 128x128 states: every pair;
-* the backward of the 64-head layer (heads {0, 21, 42, 63}) and the sequence-split backward of
-  65,536 tokens x 8 heads (all heads), against the oracle's two-scan gradient form.
+* the sequence-split backward of 65,536 tokens x 8 heads (all heads) against the oracle's
+  two-scan gradient form (the 64-head backward is in test_gpu_backward.py).
 """
 import numpy as np
 import pytest
@@ -135,22 +135,6 @@ def _check_grads(got, want, T, what):
         print("%s %s: max rel-L2 %.2e" % (what, name, e.max()), flush=True)
         worst = max(worst, float(e.max()))
     assert worst <= BF16_TOL, "%s: %.3e" % (what, worst)
-
-
-def test_backward_64k_sampled_heads():
-    """The benchmark's backward leg: 65,536 tokens x 64 heads, plain; heads {0, 21, 42, 63}
-    against O7."""
-    wl = synth.workloads()["prefill_64k"]
-    banner("backward prefill_64k T=65536 H=64 D=128 bf16")
-    q, k, v = wl.inputs(device="cuda")
-    do, _, _ = synth.qkv(wl.T, wl.H, wl.D, torch.bfloat16, seed=50, device="cuda")
-    decay = wl.decay()
-    dq, dk, dv, _ = la.backward(q, k, v, decay.to(dev()), do, want_d_initial_state=False)
-    torch.cuda.synchronize()
-    hs = SAMPLED_HEADS
-    want = oracle.backward_recurrent(_heads(q, hs), _heads(k, hs), _heads(v, hs), decay[hs],
-                                     _heads(do, hs), want_d_init=False)
-    _check_grads([_heads(x, hs) for x in (dq, dk, dv)], want[:3], wl.T, "backward 64k")
 
 
 def test_backward_split_64k_8_heads():
