@@ -1,22 +1,360 @@
-// prefill_f32.hip -- lightning-attention prefill with fp32 storage and fp32 arithmetic.
+// prefill_f32.hip -- lightning-attention prefill with fp32 storage and fp32 arithmetic (gfx950).
 //
 // Same block algorithm as the bf16 MFMA path ("MiniMax-01 technical report digest",
 // futurefh.com, section 1: intra-block left product, inter-block right product over a running
-// state), computed with fp32 FMAs from LDS so that fp32 inputs keep fp32 accuracy end to end.
+// state), computed with fp32 matrix instructions (v_mfma_f32_16x16x4_f32: fp32 operands,
+// products and accumulation) so that fp32 inputs keep fp32 accuracy end to end.
 // For block i of b rows (rows j, KV_{-1} = initial state):
 //   O_i  = ((Q_i K_i^T) * M) V_i + diag(lambda^(j+1)) Q_i KV_{i-1},  M[j][j'] = lambda^(j-j') [j' <= j]
 //   KV_i = lambda^b KV_{i-1} + K_i^T diag(lambda^(b-1-j)) V_i
-// One workgroup per (sequence, head, 32-column value slice); the state slice lives in LDS.
+// One workgroup per (sequence, head, 32-column value slice), eight waves.  Output wave r owns
+// rows 16r..16r+15 of every block (scores on its r+1 causal 16x16 key tiles, decay mask, inter
+// and intra products, store); state wave r holds a share of the 16x16 tiles of the fp32 state
+// slice in registers for the whole sequence.  Output wave r and state wave r run on the same
+// SIMD, and the state tiles are dealt so that every SIMD issues about the same number of matrix
+// instructions per block; each wave's LDS waits are covered by the other wave's matrix work.
+// A block is staged row-major in LDS (Q, K and the slice of V) together with a transposed copy
+// of the state for the inter product; the next block's global loads are in flight in registers
+// while the current one is computed.
+//
+// Operand layout of v_mfma_f32_16x16x4_f32 (64 lanes, lane l: g = l/16, c = l%16): lane l
+// supplies A[c][k_g] and B[k_g][c] and holds C[4g+i][c], i = 0..3.  Any choice of the k-index
+// k_g that A and B share gives the same product, so four instructions consume elements
+// m = 0..3 of one 16-byte LDS read per lane with k_g = 4g + m inside a 16-element chunk.  The
+// score accumulator (lane holds S^T[key 16t + 4g + i][row c]) is then exactly the B operand of
+// the intra product with k = key, so the masked scores never leave registers.
+//
 // Variants (flags): a reversed scan (local token t = physical token n-1-t), an initial state
-// weighted lambda^t with the final state times lambda, a transposed initial state, and a
-// state-only pass that reads no q and writes no out.
+// weighted lambda^t with the final state times lambda (only for sequences s with
+// incl_v[s] != 0 when incl_v is given), a transposed initial state, and a state-only pass that
+// reads no q and writes no out.
 #include "la_internal.h"
 
 namespace {
 
 constexpr int BLK = 64;
 constexpr int CV = 32;
-constexpr int NTHR = 256;
+constexpr int NTHR = 512;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// State tiles of a slice (16 key features x 16 value columns; tile x covers features
+// 16 (x/2).. and columns 16 (x%2)..) dealt to the state waves.  State wave r shares a SIMD with
+// output wave r, which computes r+1 score tiles, so the low waves take more state tiles.
+template <int D>
+struct Tiles {
+  static constexpr int count(int r) {
+    return D == 128 ? (r == 0 ? 8 : r == 1 ? 5 : r == 2 ? 3 : 0)
+                    : (r == 0 ? 4 : r == 1 ? 3 : r == 2 ? 1 : 0);
+  }
+  static constexpr int first(int r) { return r == 0 ? 0 : first(r - 1) + count(r - 1); }
+  static_assert(first(4) == (D / 16) * (CV / 16), "every state tile dealt once");
+};
+
+// LDS image of one block.  Row pitches are chosen so that the 16 lanes that read one 16-byte
+// column of 16 consecutive rows, and the lanes that read one float of rows 4 apart, fall on
+// distinct banks.
+template <int D>
+struct Smem {
+  static constexpr int QP = D + 4;
+  static constexpr int VP = CV + 4;
+  float q[BLK][QP];    // Q rows of the block (zeros past b)
+  float k[BLK][QP];    // K rows
+  float v[BLK][VP];    // V[j][c0 + c]
+  float kvt[CV][QP];   // kvt[c][a] = KV[a][c0 + c], the state the block's rows see
+  float pw[BLK + 4];   // lambda^m, m = 0..BLK
+};
+
+struct Ctx {
+  const float *q, *k, *v;  // (first token of the sequence, head h)
+  float *out;              // (first token, head h, column c0)
+  int64_t n;
+  int64_t rowstride;       // H * D elements between tokens
+  int c0;
+  bool rev, incl, s0t, so;
+
+  // Element offset of the first row of the block that starts at local token i0; local row j of
+  // the block sits j * rowstride after it (before it when the scan is reversed).
+  __device__ __forceinline__ int64_t block_base(int64_t i0) const {
+    return (rev ? n - 1 - i0 : i0) * rowstride;
+  }
+  __device__ __forceinline__ int row_off(int j) const {
+    return (rev ? -j : j) * (int)rowstride;
+  }
+};
+
+// One block's rows held in registers between the global loads and the LDS stores.  Thread tid
+// carries element chunks e = tid + u * NTHR: Q/K row e / (D/4), features 4 (e % (D/4)).. and
+// V row e / (CV/4), columns 4 (e % (CV/4))...  The per-lane offsets inside a block are fixed.
+template <int D>
+struct Staged {
+  static constexpr int NQK = BLK * D / 4 / NTHR;
+  static constexpr int NV = BLK * CV / 4 / NTHR;
+  static constexpr int Q4 = D / 4, V4 = CV / 4;
+  f32x4 q[NQK], k[NQK], v[NV];
+  int oqk[NQK], ov[NV];
+
+  __device__ __forceinline__ void init(const Ctx &x, int tid) {
+#pragma unroll
+    for (int u = 0; u < NQK; ++u) {
+      const int e = tid + u * NTHR;
+      oqk[u] = x.row_off(e / Q4) + 4 * (e % Q4);
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + u * NTHR;
+      ov[u] = x.row_off(e / V4) + x.c0 + 4 * (e % V4);
+    }
+  }
+
+  // Rows j >= b of a partial block are zero-filled.
+  __device__ __forceinline__ void fetch(const Ctx &x, int64_t i0, int b, int tid) {
+    const int64_t base = x.block_base(i0);
+    const float *pk = x.k + base, *pq = x.q + base, *pv = x.v + base;
+    if (b == BLK) {
+#pragma unroll
+      for (int u = 0; u < NQK; ++u) k[u] = *(const f32x4 *)(pk + oqk[u]);
+      if (!x.so) {
+#pragma unroll
+        for (int u = 0; u < NQK; ++u) q[u] = *(const f32x4 *)(pq + oqk[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) v[u] = *(const f32x4 *)(pv + ov[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NQK; ++u) {
+        const bool in = (tid + u * NTHR) / Q4 < b;
+        k[u] = q[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (in) k[u] = *(const f32x4 *)(pk + oqk[u]);
+        if (in && !x.so) q[u] = *(const f32x4 *)(pq + oqk[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if ((tid + u * NTHR) / V4 < b) v[u] = *(const f32x4 *)(pv + ov[u]);
+      }
+    }
+    if (x.so) {
+#pragma unroll
+      for (int u = 0; u < NQK; ++u) q[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  __device__ __forceinline__ void commit(Smem<D> &sm, int tid) const {
+#pragma unroll
+    for (int u = 0; u < NQK; ++u) {
+      const int e = tid + u * NTHR, j = e / Q4, a = 4 * (e % Q4);
+      *(f32x4 *)&sm.q[j][a] = q[u];
+      *(f32x4 *)&sm.k[j][a] = k[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + u * NTHR, j = e / V4, cc = 4 * (e % V4);
+      *(f32x4 *)&sm.v[j][cc] = v[u];
+    }
+  }
+};
+
+// Output wave r: rows 16r..16r+15 of every block.
+template <int D, int R>
+__device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) {
+  constexpr int NT = R + 1;  // causal score tiles of the wave's rows
+  constexpr int NQ = D / 16; // 16-feature chunks
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int jrow = 16 * R + c;  // the lane's output row inside a block
+
+  Staged<D> st;
+  st.init(x, tid);
+  st.fetch(x, 0, (int)(x.n < BLK ? x.n : BLK), tid);
+  st.commit(sm, tid);
+  __syncthreads();
+
+  // Per-lane weights that are the same for every block: the decay mask of the lane's score
+  // entries (lambda^(row - key), exactly 0 above the diagonal) and the inter scale of its row.
+  float mw[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 16 * t + 4 * g + i;
+      mw[t][i] = key <= jrow ? sm.pw[key <= jrow ? jrow - key : 0] : 0.f;
+    }
+  const float isc_incl = sm.pw[jrow], isc_full = sm.pw[jrow + 1];
+  float *const out_lane = x.out + x.row_off(jrow) + 4 * g;
+
+  for (int64_t i0 = 0; i0 < x.n; i0 += BLK) {
+    const int b = (int)(x.n - i0 < BLK ? x.n - i0 : BLK);
+    const int64_t i1 = i0 + BLK;
+    if (i1 < x.n) st.fetch(x, i1, (int)(x.n - i1 < BLK ? x.n - i1 : BLK), tid);
+
+    if (!x.so) {
+      f32x4 qop[NQ];
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) qop[qq] = *(const f32x4 *)&sm.q[jrow][16 * qq + 4 * g];
+      // sacc[t][i] = S^T[16t + 4g + i][jrow] = K[16t + 4g + i] . Q[jrow]
+      f32x4 sacc[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const f32x4 kop = *(const f32x4 *)&sm.k[16 * t + c][16 * qq + 4 * g];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) sacc[t] = mfma4(kop[m], qop[qq][m], sacc[t]);
+        }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * t + 4 * g + i;
+          sacc[t][i] = key <= jrow ? sacc[t][i] * mw[t][i] : 0.f;
+        }
+      // Inter part: o[ct][i] = sum_a KV[a][c0 + 16ct + 4g + i] Q[jrow][a].
+      f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const f32x4 kvo = *(const f32x4 *)&sm.kvt[16 * ct + c][16 * qq + 4 * g];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) o[ct] = mfma4(kvo[m], qop[qq][m], o[ct]);
+        }
+      const float isc = i0 == 0 && x.incl ? isc_incl : isc_full;
+      o[0] *= isc;
+      o[1] *= isc;
+      // Intra part: o[ct][i] += sum_key V[key][c0 + 16ct + 4g + i] P[jrow][key].
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            o[ct] = mfma4(sm.v[16 * t + 4 * g + m][16 * ct + c], sacc[t][m], o[ct]);
+      if (jrow < b) {
+        float *dst = out_lane + x.block_base(i0);
+        *(f32x4 *)dst = o[0];
+        *(f32x4 *)(dst + 16) = o[1];
+      }
+    }
+    __syncthreads();  // every read of this block's rows and of the state copy is done
+    if (i1 < x.n) {
+      st.commit(sm, tid);
+      __syncthreads();
+    }
+  }
+}
+
+// State wave r: its share of the 16x16 tiles of the state slice, in registers for the whole
+// sequence; publishes the transposed copy the output waves read.
+template <int D, int R>
+__device__ __forceinline__ void state_wave(const Ctx &x, Smem<D> &sm, const float *s0, float *fs,
+                                          size_t sbase, int tid) {
+  using TL = Tiles<D>;
+  constexpr int NTL = TL::count(R);
+  constexpr int T0 = TL::first(R);
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+
+  // kv[t][i] = KV[16 rt + 4g + i][c0 + 16 ct + c] for tile T0 + t (rt = tile / 2, ct = tile % 2).
+  f32x4 kv[NTL > 0 ? NTL : 1];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    const int rt = (T0 + t) / 2, ct = (T0 + t) % 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int a = 16 * rt + 4 * g + i, dv = x.c0 + 16 * ct + c;
+      kv[t][i] = s0 ? s0[sbase + (x.s0t ? (size_t)dv * D + a : (size_t)a * D + dv)] : 0.f;
+    }
+  }
+  auto write_kvt = [&]() {
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const int rt = (T0 + t) / 2, ct = (T0 + t) % 2;
+      *(f32x4 *)&sm.kvt[16 * ct + c][16 * rt + 4 * g] = kv[t];
+    }
+  };
+
+  Staged<D> st;
+  st.init(x, tid);
+  st.fetch(x, 0, (int)(x.n < BLK ? x.n : BLK), tid);
+  st.commit(sm, tid);
+  write_kvt();
+  __syncthreads();
+
+  // State weights lambda^(BLK-1-j) of the rows j the lane feeds to the state product, and the
+  // decay of the state over a full block, the same for every full block.
+  float wf[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) wf[s][m] = sm.pw[BLK - 1 - (16 * s + 4 * g + m)];
+  const float lam_b = sm.pw[BLK], lam_b1 = sm.pw[BLK - 1];
+
+  for (int64_t i0 = 0; i0 < x.n; i0 += BLK) {
+    const int b = (int)(x.n - i0 < BLK ? x.n - i0 : BLK);
+    const bool first = i0 == 0;
+    const int64_t i1 = i0 + BLK;
+    if (i1 < x.n) st.fetch(x, i1, (int)(x.n - i1 < BLK ? x.n - i1 : BLK), tid);
+
+    // KV = lambda^b KV + K^T diag(lambda^(b-1-j)) V, with lambda^(b-1) in place of lambda^b on
+    // an inclusive initial state's first block.  Rows past b are zero in LDS and weighted 0.
+    if constexpr (NTL > 0) {
+      float w[4][4], lb;
+      if (b == BLK) {
+        lb = first && x.incl ? lam_b1 : lam_b;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) w[s][m] = wf[s][m];
+      } else {
+        lb = first && x.incl ? sm.pw[b - 1] : sm.pw[b];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int e = b - 1 - (16 * s + 4 * g + m);
+            w[s][m] = e >= 0 ? sm.pw[e >= 0 ? e : 0] : 0.f;
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) kv[t] *= lb;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int j = 16 * s + 4 * g + m;
+#pragma unroll
+          for (int t = 0; t < NTL; ++t) {
+            const int rt = (T0 + t) / 2, ct = (T0 + t) % 2;
+            kv[t] = mfma4(sm.k[j][16 * rt + c], w[s][m] * sm.v[j][16 * ct + c], kv[t]);
+          }
+        }
+    }
+    __syncthreads();  // every read of this block's rows and of the state copy is done
+    if (i1 < x.n) {
+      st.commit(sm, tid);
+      write_kvt();
+      __syncthreads();
+    }
+  }
+
+  if (fs) {
+    const float fsc = x.incl && x.n > 0 ? sm.pw[1] : 1.f;
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const int rt = (T0 + t) / 2, ct = (T0 + t) % 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = 16 * rt + 4 * g + i, dv = x.c0 + 16 * ct + c;
+        fs[sbase + (size_t)a * D + dv] = kv[t][i] * fsc;
+      }
+    }
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(NTHR) void prefill_f32_kernel(
@@ -24,90 +362,45 @@ __global__ __launch_bounds__(NTHR) void prefill_f32_kernel(
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ fs, int64_t T,
     int H, int flags, const int32_t *__restrict__ incl_v) {
-  const bool rev = flags & 1, s0t = flags & 4, so = flags & 8;
   constexpr int NS = D / CV;
-  __shared__ float Qs[BLK][D + 1];
-  __shared__ float Ks[BLK][D + 1];
-  __shared__ float Vs[BLK][CV + 1];
-  __shared__ float Ps[BLK][BLK + 1];
-  __shared__ float KV[D][CV + 1];
-  __shared__ float pw[BLK + 1];
-
+  __shared__ __attribute__((aligned(16))) Smem<D> sm;
   const int chain = blockIdx.x / NS, slice = blockIdx.x % NS;
   const int seq = chain / H, h = chain % H;
-  const bool incl = (flags & 2) && (incl_v == nullptr || incl_v[seq] != 0);
   const int64_t tok0 = cu ? (int64_t)cu[seq] : 0;
   const int64_t tok1 = cu ? (int64_t)cu[seq + 1] : T;
-  const int64_t n = tok1 > tok0 ? tok1 - tok0 : 0;
-  const int c0 = slice * CV;
+  Ctx x;
+  x.n = tok1 > tok0 ? tok1 - tok0 : 0;
+  x.rowstride = (int64_t)H * D;
+  const int64_t first = (tok0 * H + h) * D;
+  x.q = q + first;
+  x.k = k + first;
+  x.v = v + first;
+  x.c0 = slice * CV;
+  x.out = out + first + x.c0;
+  x.rev = flags & 1;
+  x.incl = (flags & 2) && (incl_v == nullptr || incl_v[seq] != 0);
+  x.s0t = flags & 4;
+  x.so = flags & 8;
   const int tid = threadIdx.x;
-  const float lam = decay[h];
   if (tid <= BLK) {
-    double p = 1.0;
+    const float lam = decay[h];
+    double p = 1.0;  // lambda^tid by repeated multiplication (0^0 = 1)
     for (int i = 0; i < tid; ++i) p *= (double)lam;
-    pw[tid] = (float)p;
+    sm.pw[tid] = (float)p;
   }
+  // pw is made visible by the barrier that follows the first block's staging.
   const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
-  for (int e = tid; e < D * CV; e += NTHR) {
-    const int a = e / CV, c = e % CV;
-    KV[a][c] = s0 ? s0[sbase + (s0t ? (size_t)(c0 + c) * D + a : (size_t)a * D + c0 + c)] : 0.f;
-  }
-  __syncthreads();
-
-  // Physical token of local token t.
-  auto tok = [&](int64_t t) { return tok0 + (rev ? n - 1 - t : t); };
-  for (int64_t i0 = 0; i0 < n; i0 += BLK) {
-    const int b = (int)(n - i0 < BLK ? n - i0 : BLK);
-    for (int e = tid; e < BLK * D; e += NTHR) {
-      const int j = e / D, d = e % D;
-      const int64_t off = j < b ? (tok(i0 + j) * H + h) * (int64_t)D + d : 0;
-      Qs[j][d] = j < b && !so ? q[off] : 0.f;
-      Ks[j][d] = j < b ? k[off] : 0.f;
-    }
-    for (int e = tid; e < BLK * CV; e += NTHR) {
-      const int j = e / CV, c = e % CV;
-      Vs[j][c] = j < b ? v[(tok(i0 + j) * H + h) * (int64_t)D + c0 + c] : 0.f;
-    }
-    __syncthreads();
-    if (!so) {
-      // Masked, decayed scores (select: entries above the diagonal are exactly zero).
-      for (int e = tid; e < BLK * BLK; e += NTHR) {
-        const int j = e / BLK, jp = e % BLK;
-        float s = 0.f;
-        if (jp <= j && j < b) {
-          for (int d = 0; d < D; ++d) s = fmaf(Qs[j][d], Ks[jp][d], s);
-          s *= pw[j - jp];
-        }
-        Ps[j][jp] = s;
-      }
-      __syncthreads();
-      // Outputs: inter (right product with the previous state) + intra (left product).
-      for (int e = tid; e < BLK * CV; e += NTHR) {
-        const int j = e / CV, c = e % CV;
-        if (j >= b) continue;
-        float inter = 0.f;
-        for (int a = 0; a < D; ++a) inter = fmaf(Qs[j][a], KV[a][c], inter);
-        float intra = 0.f;
-        for (int jp = 0; jp <= j; ++jp) intra = fmaf(Ps[j][jp], Vs[jp][c], intra);
-        const float isc = i0 == 0 && incl ? pw[j] : pw[j + 1];
-        out[(tok(i0 + j) * H + h) * (int64_t)D + c0 + c] = fmaf(isc, inter, intra);
-      }
-      __syncthreads();
-    }  // !so
-    // State update.
-    for (int e = tid; e < D * CV; e += NTHR) {
-      const int a = e / CV, c = e % CV;
-      float acc = 0.f;
-      for (int j = 0; j < b; ++j) acc = fmaf(pw[b - 1 - j] * Ks[j][a], Vs[j][c], acc);
-      KV[a][c] = fmaf(i0 == 0 && incl ? pw[b - 1] : pw[b], KV[a][c], acc);
-    }
-    __syncthreads();
-  }
-  if (fs) {
-    for (int e = tid; e < D * CV; e += NTHR) {
-      const int a = e / CV, c = e % CV;
-      fs[sbase + (size_t)a * D + c0 + c] = incl && n > 0 ? KV[a][c] * pw[1] : KV[a][c];
-    }
+  // Waves w and w + 4 share a SIMD: output wave r pairs with the state wave holding the most
+  // tiles where r has the fewest score tiles.
+  switch (__builtin_amdgcn_readfirstlane(tid >> 6)) {
+    case 0: output_wave<D, 0>(x, sm, tid); break;
+    case 1: output_wave<D, 1>(x, sm, tid); break;
+    case 2: output_wave<D, 2>(x, sm, tid); break;
+    case 3: output_wave<D, 3>(x, sm, tid); break;
+    case 4: state_wave<D, 0>(x, sm, s0, fs, sbase, tid); break;
+    case 5: state_wave<D, 1>(x, sm, s0, fs, sbase, tid); break;
+    case 6: state_wave<D, 2>(x, sm, s0, fs, sbase, tid); break;
+    default: state_wave<D, 3>(x, sm, s0, fs, sbase, tid); break;
   }
 }
 
