@@ -55,18 +55,18 @@ struct Tiles {
   static_assert(first(4) == (D / 16) * (CV / 16), "every state tile dealt once");
 };
 
-// LDS image of one block.  Row pitches are chosen so that the 16 lanes that read one 16-byte
-// column of 16 consecutive rows, and the lanes that read one float of rows 4 apart, fall on
-// distinct banks.
+// LDS: two buffers of a block's K rows and V slice, and two transposed copies of the state,
+// so that block i+1 is staged while block i is read.  Row pitches are chosen so that the 16
+// lanes that read one 16-byte column of 16 consecutive rows, and the lanes that read one float
+// of rows 4 apart, fall on distinct banks.
 template <int D>
 struct Smem {
-  static constexpr int QP = D + 4;
+  static constexpr int KP = D + 4;
   static constexpr int VP = CV + 4;
-  float q[BLK][QP];    // Q rows of the block (zeros past b)
-  float k[BLK][QP];    // K rows
-  float v[BLK][VP];    // V[j][c0 + c]
-  float kvt[CV][QP];   // kvt[c][a] = KV[a][c0 + c], the state the block's rows see
-  float pw[BLK + 4];   // lambda^m, m = 0..BLK
+  float k[2][BLK][KP];   // K rows (zeros past b)
+  float v[2][BLK][VP];   // V[j][c0 + c]
+  float kvt[2][CV][KP];  // kvt[c][a] = KV[a][c0 + c], the state the block's rows see
+  float pw[BLK + 4];     // lambda^m, m = 0..BLK
 };
 
 struct Ctx {
@@ -85,92 +85,96 @@ struct Ctx {
   __device__ __forceinline__ int row_off(int j) const {
     return (rev ? -j : j) * (int)rowstride;
   }
+  __device__ __forceinline__ int rows(int64_t i0) const {
+    return (int)(n - i0 < BLK ? n - i0 : BLK);
+  }
 };
 
-// One block's rows held in registers between the global loads and the LDS stores.  Thread tid
-// carries element chunks e = tid + u * NTHR: Q/K row e / (D/4), features 4 (e % (D/4)).. and
-// V row e / (CV/4), columns 4 (e % (CV/4))...  The per-lane offsets inside a block are fixed.
+// One block's K rows and V slice held in registers between the global loads and the LDS
+// stores.  Thread tid carries element chunks e = tid + u * NTHR: K row e / (D/4), features
+// 4 (e % (D/4)).. and V row e / (CV/4), columns 4 (e % (CV/4))...  The loads are
+// unconditional, so that they stay in flight while a block is computed: rows past the end of a
+// partial block re-read its last row and are zeroed when they are stored to LDS.
 template <int D>
 struct Staged {
-  static constexpr int NQK = BLK * D / 4 / NTHR;
+  static constexpr int NK = BLK * D / 4 / NTHR;
   static constexpr int NV = BLK * CV / 4 / NTHR;
-  static constexpr int Q4 = D / 4, V4 = CV / 4;
-  f32x4 q[NQK], k[NQK], v[NV];
-  int oqk[NQK], ov[NV];
+  static constexpr int K4 = D / 4, V4 = CV / 4;
+  f32x4 k[NK], v[NV];
+  int b;  // rows of the staged block
 
-  __device__ __forceinline__ void init(const Ctx &x, int tid) {
-#pragma unroll
-    for (int u = 0; u < NQK; ++u) {
-      const int e = tid + u * NTHR;
-      oqk[u] = x.row_off(e / Q4) + 4 * (e % Q4);
-    }
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = tid + u * NTHR;
-      ov[u] = x.row_off(e / V4) + x.c0 + 4 * (e % V4);
-    }
-  }
-
-  // Rows j >= b of a partial block are zero-filled.
-  __device__ __forceinline__ void fetch(const Ctx &x, int64_t i0, int b, int tid) {
+  // Block of rows >= 1 rows starting at local token i0.
+  __device__ __forceinline__ void fetch(const Ctx &x, int64_t i0, int rows, int tid) {
+    b = rows;
     const int64_t base = x.block_base(i0);
-    const float *pk = x.k + base, *pq = x.q + base, *pv = x.v + base;
-    if (b == BLK) {
+    const float *pk = x.k + base, *pv = x.v + base;
 #pragma unroll
-      for (int u = 0; u < NQK; ++u) k[u] = *(const f32x4 *)(pk + oqk[u]);
-      if (!x.so) {
-#pragma unroll
-        for (int u = 0; u < NQK; ++u) q[u] = *(const f32x4 *)(pq + oqk[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) v[u] = *(const f32x4 *)(pv + ov[u]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < NQK; ++u) {
-        const bool in = (tid + u * NTHR) / Q4 < b;
-        k[u] = q[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (in) k[u] = *(const f32x4 *)(pk + oqk[u]);
-        if (in && !x.so) q[u] = *(const f32x4 *)(pq + oqk[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if ((tid + u * NTHR) / V4 < b) v[u] = *(const f32x4 *)(pv + ov[u]);
-      }
-    }
-    if (x.so) {
-#pragma unroll
-      for (int u = 0; u < NQK; ++u) q[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-
-  __device__ __forceinline__ void commit(Smem<D> &sm, int tid) const {
-#pragma unroll
-    for (int u = 0; u < NQK; ++u) {
-      const int e = tid + u * NTHR, j = e / Q4, a = 4 * (e % Q4);
-      *(f32x4 *)&sm.q[j][a] = q[u];
-      *(f32x4 *)&sm.k[j][a] = k[u];
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + u * NTHR, j = e / K4;
+      k[u] = *(const f32x4 *)(pk + x.row_off(j < rows ? j : rows - 1) + 4 * (e % K4));
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int e = tid + u * NTHR, j = e / V4, cc = 4 * (e % V4);
-      *(f32x4 *)&sm.v[j][cc] = v[u];
+      const int e = tid + u * NTHR, j = e / V4;
+      v[u] = *(const f32x4 *)(pv + x.row_off(j < rows ? j : rows - 1) + x.c0 + 4 * (e % V4));
     }
+  }
+
+  __device__ __forceinline__ void commit(Smem<D> &sm, int buf, int tid) const {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + u * NTHR, j = e / K4;
+      *(f32x4 *)&sm.k[buf][j][4 * (e % K4)] = j < b ? k[u] : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + u * NTHR, j = e / V4;
+      *(f32x4 *)&sm.v[buf][j][4 * (e % V4)] = j < b ? v[u] : zero;
+    }
+  }
+
+  // Loads for the block at i0, or past the last block for the last block again (its rows are
+  // then never stored).
+  __device__ __forceinline__ void fetch_or_last(const Ctx &x, int64_t i0, int64_t ilast,
+                                                int tid) {
+    const int64_t ib = i0 < x.n ? i0 : ilast;
+    fetch(x, ib, x.rows(ib), tid);
   }
 };
 
-// Output wave r: rows 16r..16r+15 of every block.
+// Block pipeline shared by both kinds of wave.  Before the loop: block 0 staged in buffer 0,
+// block 1's loads in flight.  In step i (buffer p = i % 2): compute block i from buffer p; store
+// block i+1 to buffer 1-p, which was last read in step i-1; issue the loads of block i+2; one
+// barrier.  The state waves publish the state after block i into the state copy 1-p.
+//
+// Output wave r: rows 16r..16r+15 of every block; its Q rows are loaded straight into
+// registers, one block ahead.
 template <int D, int R>
 __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) {
-  constexpr int NT = R + 1;  // causal score tiles of the wave's rows
-  constexpr int NQ = D / 16; // 16-feature chunks
+  constexpr int NT = R + 1;   // causal score tiles of the wave's rows
+  constexpr int NQ = D / 16;  // 16-feature chunks
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int jrow = 16 * R + c;  // the lane's output row inside a block
+  const int64_t ilast = x.n > 0 ? (x.n - 1) / BLK * BLK : 0;
+
+  // Q[jrow][16qq + 4g .. + 3] of the block at i0 (its last row for rows past a partial block;
+  // those outputs are not stored).
+  auto load_q = [&](f32x4 *dst, int64_t i0) {
+    const int b = x.rows(i0);
+    const float *pq = x.q + x.block_base(i0) + x.row_off(jrow < b ? jrow : b - 1) + 4 * g;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) dst[qq] = *(const f32x4 *)(pq + 16 * qq);
+  };
 
   Staged<D> st;
-  st.init(x, tid);
-  st.fetch(x, 0, (int)(x.n < BLK ? x.n : BLK), tid);
-  st.commit(sm, tid);
+  f32x4 qop[NQ];
+  if (x.n > 0) {
+    st.fetch(x, 0, x.rows(0), tid);
+    if (!x.so) load_q(qop, 0);
+    st.commit(sm, 0, tid);
+    st.fetch_or_last(x, BLK, ilast, tid);
+  }
   __syncthreads();
 
   // Per-lane weights that are the same for every block: the decay mask of the lane's score
@@ -186,15 +190,14 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
   const float isc_incl = sm.pw[jrow], isc_full = sm.pw[jrow + 1];
   float *const out_lane = x.out + x.row_off(jrow) + 4 * g;
 
-  for (int64_t i0 = 0; i0 < x.n; i0 += BLK) {
-    const int b = (int)(x.n - i0 < BLK ? x.n - i0 : BLK);
+  int p = 0;
+  for (int64_t i0 = 0; i0 < x.n; i0 += BLK, p ^= 1) {
+    const int b = x.rows(i0);
     const int64_t i1 = i0 + BLK;
-    if (i1 < x.n) st.fetch(x, i1, (int)(x.n - i1 < BLK ? x.n - i1 : BLK), tid);
 
     if (!x.so) {
-      f32x4 qop[NQ];
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) qop[qq] = *(const f32x4 *)&sm.q[jrow][16 * qq + 4 * g];
+      f32x4 qnext[NQ];
+      load_q(qnext, i1 < x.n ? i1 : i0);
       // sacc[t][i] = S^T[16t + 4g + i][jrow] = K[16t + 4g + i] . Q[jrow]
       f32x4 sacc[NT];
 #pragma unroll
@@ -203,7 +206,7 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
       for (int qq = 0; qq < NQ; ++qq)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const f32x4 kop = *(const f32x4 *)&sm.k[16 * t + c][16 * qq + 4 * g];
+          const f32x4 kop = *(const f32x4 *)&sm.k[p][16 * t + c][16 * qq + 4 * g];
 #pragma unroll
           for (int m = 0; m < 4; ++m) sacc[t] = mfma4(kop[m], qop[qq][m], sacc[t]);
         }
@@ -220,7 +223,7 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
       for (int qq = 0; qq < NQ; ++qq)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const f32x4 kvo = *(const f32x4 *)&sm.kvt[16 * ct + c][16 * qq + 4 * g];
+          const f32x4 kvo = *(const f32x4 *)&sm.kvt[p][16 * ct + c][16 * qq + 4 * g];
 #pragma unroll
           for (int m = 0; m < 4; ++m) o[ct] = mfma4(kvo[m], qop[qq][m], o[ct]);
         }
@@ -234,18 +237,18 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            o[ct] = mfma4(sm.v[16 * t + 4 * g + m][16 * ct + c], sacc[t][m], o[ct]);
+            o[ct] = mfma4(sm.v[p][16 * t + 4 * g + m][16 * ct + c], sacc[t][m], o[ct]);
       if (jrow < b) {
         float *dst = out_lane + x.block_base(i0);
         *(f32x4 *)dst = o[0];
         *(f32x4 *)(dst + 16) = o[1];
       }
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) qop[qq] = qnext[qq];
     }
-    __syncthreads();  // every read of this block's rows and of the state copy is done
-    if (i1 < x.n) {
-      st.commit(sm, tid);
-      __syncthreads();
-    }
+    if (i1 < x.n) st.commit(sm, p ^ 1, tid);
+    st.fetch_or_last(x, i1 + BLK, ilast, tid);
+    __syncthreads();  // block i+1 staged; every read of buffer p done
   }
 }
 
@@ -258,6 +261,7 @@ __device__ __forceinline__ void state_wave(const Ctx &x, Smem<D> &sm, const floa
   constexpr int NTL = TL::count(R);
   constexpr int T0 = TL::first(R);
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int64_t ilast = x.n > 0 ? (x.n - 1) / BLK * BLK : 0;
 
   // kv[t][i] = KV[16 rt + 4g + i][c0 + 16 ct + c] for tile T0 + t (rt = tile / 2, ct = tile % 2).
   f32x4 kv[NTL > 0 ? NTL : 1];
@@ -270,19 +274,21 @@ __device__ __forceinline__ void state_wave(const Ctx &x, Smem<D> &sm, const floa
       kv[t][i] = s0 ? s0[sbase + (x.s0t ? (size_t)dv * D + a : (size_t)a * D + dv)] : 0.f;
     }
   }
-  auto write_kvt = [&]() {
+  auto write_kvt = [&](int buf) {
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
       const int rt = (T0 + t) / 2, ct = (T0 + t) % 2;
-      *(f32x4 *)&sm.kvt[16 * ct + c][16 * rt + 4 * g] = kv[t];
+      *(f32x4 *)&sm.kvt[buf][16 * ct + c][16 * rt + 4 * g] = kv[t];
     }
   };
 
   Staged<D> st;
-  st.init(x, tid);
-  st.fetch(x, 0, (int)(x.n < BLK ? x.n : BLK), tid);
-  st.commit(sm, tid);
-  write_kvt();
+  if (x.n > 0) {
+    st.fetch(x, 0, x.rows(0), tid);
+    st.commit(sm, 0, tid);
+    st.fetch_or_last(x, BLK, ilast, tid);
+  }
+  write_kvt(0);
   __syncthreads();
 
   // State weights lambda^(BLK-1-j) of the rows j the lane feeds to the state product, and the
@@ -294,11 +300,11 @@ __device__ __forceinline__ void state_wave(const Ctx &x, Smem<D> &sm, const floa
     for (int m = 0; m < 4; ++m) wf[s][m] = sm.pw[BLK - 1 - (16 * s + 4 * g + m)];
   const float lam_b = sm.pw[BLK], lam_b1 = sm.pw[BLK - 1];
 
-  for (int64_t i0 = 0; i0 < x.n; i0 += BLK) {
-    const int b = (int)(x.n - i0 < BLK ? x.n - i0 : BLK);
+  int p = 0;
+  for (int64_t i0 = 0; i0 < x.n; i0 += BLK, p ^= 1) {
+    const int b = x.rows(i0);
     const bool first = i0 == 0;
     const int64_t i1 = i0 + BLK;
-    if (i1 < x.n) st.fetch(x, i1, (int)(x.n - i1 < BLK ? x.n - i1 : BLK), tid);
 
     // KV = lambda^b KV + K^T diag(lambda^(b-1-j)) V, with lambda^(b-1) in place of lambda^b on
     // an inclusive initial state's first block.  Rows past b are zero in LDS and weighted 0.
@@ -330,16 +336,16 @@ __device__ __forceinline__ void state_wave(const Ctx &x, Smem<D> &sm, const floa
 #pragma unroll
           for (int t = 0; t < NTL; ++t) {
             const int rt = (T0 + t) / 2, ct = (T0 + t) % 2;
-            kv[t] = mfma4(sm.k[j][16 * rt + c], w[s][m] * sm.v[j][16 * ct + c], kv[t]);
+            kv[t] = mfma4(sm.k[p][j][16 * rt + c], w[s][m] * sm.v[p][j][16 * ct + c], kv[t]);
           }
         }
     }
-    __syncthreads();  // every read of this block's rows and of the state copy is done
     if (i1 < x.n) {
-      st.commit(sm, tid);
-      write_kvt();
-      __syncthreads();
+      st.commit(sm, p ^ 1, tid);
+      write_kvt(p ^ 1);
     }
+    st.fetch_or_last(x, i1 + BLK, ilast, tid);
+    __syncthreads();  // block i+1 and the state after block i published; buffer p free
   }
 
   if (fs) {
@@ -364,7 +370,27 @@ __global__ __launch_bounds__(NTHR) void prefill_f32_kernel(
     int H, int flags, const int32_t *__restrict__ incl_v) {
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
-  const int chain = blockIdx.x / NS, slice = blockIdx.x % NS;
+  // Workgroup -> (chain = sequence*H + head, value slice), XCD-aware: workgroups are dealt to
+  // the 8 XCDs round-robin (wg % 8), so chain c's slices are the workgroups
+  // 8 (NS (c / 8) + s) + c % 8 and share one XCD's L2, where the chain's Q and K rows are then
+  // fetched from HBM once.  The R < 8 NS workgroups past the largest multiple of 8 NS are
+  // numbered XCD by XCD (XCD x holds R / 8 of them, one more if x < R % 8) and dealt to the
+  // remaining chains in that order.
+  const int total = (int)gridDim.x;
+  const int full = total / (8 * NS) * (8 * NS);
+  const int wg = blockIdx.x;
+  int chain, slice;
+  if (wg < full) {
+    const int loc = wg >> 3;
+    slice = loc % NS;
+    chain = (loc / NS) * 8 + (wg & 7);
+  } else {
+    const int r = wg - full, R = total - full;
+    const int xx = r & 7, per = R >> 3, rem = R & 7;
+    const int pos = xx * per + (xx < rem ? xx : rem) + (r >> 3);
+    chain = full / NS + pos / NS;
+    slice = pos % NS;
+  }
   const int seq = chain / H, h = chain % H;
   const int64_t tok0 = cu ? (int64_t)cu[seq] : 0;
   const int64_t tok1 = cu ? (int64_t)cu[seq + 1] : T;
@@ -372,7 +398,7 @@ __global__ __launch_bounds__(NTHR) void prefill_f32_kernel(
   x.n = tok1 > tok0 ? tok1 - tok0 : 0;
   x.rowstride = (int64_t)H * D;
   const int64_t first = (tok0 * H + h) * D;
-  x.q = q + first;
+  x.q = q + first;  // not read by a state-only pass
   x.k = k + first;
   x.v = v + first;
   x.c0 = slice * CV;
