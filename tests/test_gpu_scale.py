@@ -8,7 +8,10 @@
   the recurrent form;
 * one decode step for 256 sequences x 64 heads of fp32 128x128 states: every pair;
 * the sequence-split backward of 65,536 tokens x 8 heads (all heads) against the oracle's
-  two-scan gradient form (the 64-head backward is in test_gpu_backward.py).
+  two-scan gradient form (the 64-head backward is in test_gpu_backward.py);
+* the fp32-storage path at length: 2 packed sequences of 40,003 and 25,590 tokens x 8 heads
+  with initial states (prefill, plain and split), and the backward of 16,411 tokens x 4 heads
+  (plain and split), at the fp32 tolerance.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ import torch
 
 import long_context_attention_attn_amd as la
 import oracle
-from gpu_util import BF16_TOL, banner, dev, rel, slice_errors, state_errors, to_np
+from gpu_util import BF16_TOL, F32_TOL, banner, dev, rel, slice_errors, state_errors, to_np
 from long_context_attention_attn_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -151,3 +154,46 @@ def test_backward_split_64k_8_heads():
     want = oracle.backward_recurrent(q.cpu(), k.cpu(), v.cpu(), decay, do.cpu(),
                                      want_d_init=False)
     _check_grads([x.cpu() for x in (dq, dk, dv)], want[:3], T, "backward split 64k x 8")
+
+
+def test_prefill_f32_long_ragged_init():
+    """fp32 storage, 2 packed sequences with ragged tails (40,003 and 25,590 tokens) x 8 heads,
+    initial states ~ N(0, 0.1^2): every head of both sequences, outputs and final states, against
+    the recurrent form; the sequence-split prefill the same way."""
+    cu = torch.tensor([0, 40003, 65593], dtype=torch.int32)
+    T, H, D, S = 65593, 8, 128, 2
+    banner("prefill fp32 T=%d (2 sequences) H=%d D=%d with initial states" % (T, H, D))
+    q, k, v = synth.qkv(T, H, D, torch.float32, seed=11)
+    decay = synth.decay_geometric(H, 0.9, 0.9999)
+    s0 = synth.random_state(S, H, D, seed=12, scale=0.1)
+    ref, ref_s = oracle.recurrent(q, k, v, decay, cu, s0)
+    args = [x.to(dev()) for x in (q, k, v, decay)]
+    for split in (None, "auto"):
+        out, fs = la.prefill(*args, cu.to(dev()), initial_state=s0.to(dev()), split=split)
+        torch.cuda.synchronize()
+        e = slice_errors(to_np(out), ref, cu.tolist())
+        es = state_errors(to_np(fs), ref_s)
+        print("fp32 prefill split=%s: out %.2e state %.2e" % (split, e.max(), es.max()),
+              flush=True)
+        assert e.max() <= F32_TOL and es.max() <= F32_TOL, split
+
+
+def test_backward_f32_16k():
+    """fp32 storage backward, 16,411 tokens x 4 heads (a ragged tail; the fp32 kernel in its
+    reversed, state-only and inclusive-initial-state modes), plain and split, against O7."""
+    T, H, D = 16411, 4, 128
+    banner("backward fp32 T=%d H=%d D=%d" % (T, H, D))
+    q, k, v = synth.qkv(T, H, D, torch.float32, seed=13)
+    do, _, _ = synth.qkv(T, H, D, torch.float32, seed=14)
+    decay = synth.decay_geometric(H, 0.9, 0.9999)
+    want = oracle.backward_recurrent(q, k, v, decay, do, want_d_init=False)
+    args = [x.to(dev()) for x in (q, k, v, decay, do)]
+    for split in (None, 4):
+        dq, dk, dv, _ = la.backward(*args, want_d_initial_state=False, split=split)
+        torch.cuda.synchronize()
+        worst = 0.0
+        for name, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want[:3]):
+            e = slice_errors(to_np(g), w, [0, T])
+            worst = max(worst, float(e.max()))
+        print("fp32 backward split=%s: worst rel-L2 %.2e" % (split, worst), flush=True)
+        assert worst <= F32_TOL, split
