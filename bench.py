@@ -169,6 +169,8 @@ def main():
         result["backward"] = backward_leg(wl, dev)
         result["few_chain_backward"] = few_chain_backward(dev)
         result["decode_tokens"] = decode_tokens_leg(dev)
+        result["fp32_prefill"] = fp32_prefill_leg(dev)
+        result["measured_peaks"] = measured_peaks(dev)
     if not args.no_cpu_baseline:
         q, k, v = wl.inputs(device=dev)
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)
@@ -308,6 +310,51 @@ def measured_traffic():
     if hashlib.sha256(src).hexdigest() != doc.get("kernel_source_sha256"):
         return None
     return doc.get("traffic_bytes_per_launch")
+
+
+def fp32_prefill_leg(dev, iters=5, warmup=2):
+    """The fp32-storage prefill (fp32 matrix instructions) at 65,536 tokens x 64 heads x d128,
+    against the 157.3 TFLOP/s fp32 matrix peak at B = 64 accounting."""
+    import torch
+    import long_context_attention_attn_amd as la
+    from long_context_attention_attn_amd import synth
+
+    T, H, D = T_PREFILL, 64, 128
+    q, k, v = synth.qkv(T, H, D, torch.float32, seed=0, device=dev)
+    decay = synth.decay_geometric(H, 0.9, 0.9999).to(dev)
+    out = torch.empty_like(q)
+    fs = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ms = time_ms(lambda: la.prefill(q, k, v, decay, out=out, final_state=fs), iters, warmup)
+    tf = prefill_flop(T, H, D) / (ms / 1e3) / 1e12
+    return {"workload": "prefill 1 x %d tokens x %d heads x d%d fp32" % (T, H, D), "ms": ms,
+            "tokens_per_s": T / (ms / 1e3), "tflops": tf, "pct_fp32_matrix_peak": 100.0 * tf / 157.3}
+
+
+def measured_peaks(dev):
+    """Ceilings re-measured on this device beside the published ones: copies of 2 GiB (HBM
+    read + write) by device memcpy and by an elementwise kernel, and large square library GEMMs
+    (dense MFMA) in bf16 and in fp32: achievable rather than theoretical peaks."""
+    import torch
+
+    n = 1 << 31
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ms = time_ms(lambda: dst.copy_(src), 10, 2)  # device-to-device memcpy (blit kernel)
+    ms_e = time_ms(lambda: torch.mul(src, 1.0, out=dst), 10, 2)  # elementwise read + write
+    res = {"hbm_memcpy_GBps": 2 * n / (ms / 1e3) / 1e9,
+           "hbm_elementwise_copy_GBps": 2 * n / (ms_e / 1e3) / 1e9,
+           "hbm_spec_GBps": HBM_PEAK_GBPS}
+    del src, dst
+    m = 8192
+    for dt, name in ((torch.bfloat16, "bf16"), (torch.float32, "fp32")):
+        a = torch.randn(m, m, device=dev, dtype=dt)
+        b = torch.randn(m, m, device=dev, dtype=dt)
+        ms = time_ms(lambda: torch.mm(a, b), 10, 3)
+        res[name + "_gemm_%d_TFLOPs" % m] = 2.0 * m ** 3 / (ms / 1e3) / 1e12
+        del a, b
+    res["bf16_spec_TFLOPs"] = BF16_PEAK_TFLOPS
+    res["fp32_matrix_spec_TFLOPs"] = 157.3
+    return res
 
 
 def copy_probe(mib, steps, warmup):
