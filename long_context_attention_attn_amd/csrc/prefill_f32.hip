@@ -13,14 +13,15 @@
 // slice in registers for the whole sequence.  Output wave r and state wave r run on the same
 // SIMD, and the state tiles are dealt so that every SIMD issues about the same number of matrix
 // instructions per block; each wave's LDS waits are covered by the other wave's matrix work.
-// A block is staged row-major in LDS (Q, K and the slice of V) together with a transposed copy
-// of the state for the inter product; the next block's global loads are in flight in registers
-// while the current one is computed.
+// K rows and the V slice of a block are staged row-major in LDS, double-buffered together with
+// a transposed copy of the state for the inter product, so that block i+1 is stored while
+// block i is read (one barrier per block); each output wave loads its own Q rows straight into
+// registers, one block ahead.
 //
 // Operand layout of v_mfma_f32_16x16x4_f32 (64 lanes, lane l: g = l/16, c = l%16): lane l
 // supplies A[c][k_g] and B[k_g][c] and holds C[4g+i][c], i = 0..3.  Any choice of the k-index
 // k_g that A and B share gives the same product, so four instructions consume elements
-// m = 0..3 of one 16-byte LDS read per lane with k_g = 4g + m inside a 16-element chunk.  The
+// m = 0..3 of one 16-byte read per lane with k_g = 4g + m inside a 16-element chunk.  The
 // score accumulator (lane holds S^T[key 16t + 4g + i][row c]) is then exactly the B operand of
 // the intra product with k = key, so the masked scores never leave registers.
 //
