@@ -9,8 +9,11 @@ Inputs are resident in HBM before the timed region.  The timed region holds exac
 bracketed by device synchronisation; per-kernel durations come from HIP events recorded on
 the stream the kernels run on.
 
-Prints ONE JSON line.  Extra legs: the roofline of the dominant kernel (prefill) and the fp64
-CPU oracle timed on a bounded sample of the same workload (--no-cpu-baseline skips it).
+Prints ONE JSON line with the roofline of the dominant kernel (prefill) and the fp64 CPU
+oracle timed on a bounded sample of the same workload (--no-cpu-baseline skips it).  Extra
+legs, timed after the K steps (--no-extras skips them): few-chain prefill and backward, plain
+and sequence-split; the 64-head backward; multi-token decode; the fp32-storage prefill; and
+ceilings re-measured on the device (copy bandwidth, library GEMM rates).
 """
 from __future__ import annotations
 
@@ -55,16 +58,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the few-chain sequence-split timings (outside the timed steps)")
+                    help="skip the extra legs timed after the K steps")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, time a plain device-to-device copy of this "
                          "many MiB (K times); used to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
-              "build has no multi-GPU path (heads/sequences would shard with no communication; "
-              "see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X and there "
+              "is no multi-GPU path (heads and sequences would shard with no communication).  "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
