@@ -265,7 +265,7 @@ def few_chain_prefill(dev, iters=20, warmup=3):
         dec = synth.decay_geometric(Hc, 0.9, 0.9999).to(dev)
         o = torch.empty_like(q)
         f = torch.empty((1, Hc, D, D), dtype=torch.float32, device=dev)
-        seg = _lib.prefill_split_blocks(T, 1, Hc, D)
+        seg = _lib.prefill_split_blocks(T, 1, Hc, D, _lib.LA_BF16)
         plain = time_ms(lambda: la.prefill(q, k, v, dec, out=o, final_state=f), iters, warmup)
         split = time_ms(lambda: la.prefill(q, k, v, dec, out=o, final_state=f, split=seg or None),
                         iters, warmup)
@@ -290,7 +290,7 @@ def few_chain_backward(dev, iters=10, warmup=2):
     q, k, v = synth.qkv(T, Hc, D, torch.bfloat16, seed=0, device=dev)
     do, _, _ = synth.qkv(T, Hc, D, torch.bfloat16, seed=50, device=dev)
     dec = synth.decay_geometric(Hc, 0.9, 0.9999).to(dev)
-    seg = _lib.prefill_split_blocks(T, 1, Hc, D)
+    seg = _lib.prefill_split_blocks(T, 1, Hc, D, _lib.LA_BF16)
     plain = time_ms(lambda: la.backward(q, k, v, dec, do), iters, warmup)
     split = time_ms(lambda: la.backward(q, k, v, dec, do, split=seg or None), iters, warmup)
     nbytes = backward_bytes(T, Hc, D)

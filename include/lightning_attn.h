@@ -62,7 +62,7 @@ typedef enum la_status {
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 int32_t la_abi_version(void);
 
 /*
@@ -128,9 +128,17 @@ size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t 
                                        int32_t seg_blocks);
 
 /* Suggested seg_blocks for the current device: about one segment workgroup per compute unit,
- * at least 4 blocks per segment; 0 when splitting would not add parallelism (the plain launch
- * already has a workgroup per compute unit, or no sequence would be cut) or on any error. */
-int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D);
+ * at least 4 blocks per segment; 0 (use the plain scan) when splitting would not add
+ * parallelism (the plain launch already has a workgroup per compute unit, or no sequence would
+ * be cut), when a cost model of both paths (fitted to MI355X timings; the mean sequence length
+ * T / S stands in for the longest) predicts the split saves less than 10% (short sequences,
+ * where its fixed cost of four launches dominates), or on any error. */
+int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype);
+
+/* The same suggestion for a device with compute_units compute units (no device access; 0 for
+ * invalid sizes or dtype). */
+int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
+                                    int32_t compute_units);
 
 /*
  * Backward of la_prefill_ex: gradients of a loss L given dL/dout (d_out) and, optionally,

@@ -102,7 +102,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
         _check_act("final_state", final_state, torch.float32, device)
         if final_state.shape != (S, H, D, D):
             raise ValueError("final_state must be [S, H, D, D]")
-    seg_blocks = _seg_blocks(split, T, S, H, D)
+    seg_blocks = _seg_blocks(split, T, S, H, D, dtype)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), decay.data_ptr(),
             0 if cu_seqlens is None else cu_seqlens.data_ptr(),
             0 if initial_state is None else initial_state.data_ptr(),
@@ -119,10 +119,10 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
     return out, final_state
 
 
-def _seg_blocks(split, T, S, H, D) -> int:
+def _seg_blocks(split, T, S, H, D, dtype) -> int:
     """Segment length (in 64-token blocks) for ``split``; 0 = no sequence split."""
     if split == "auto":
-        return _lib.prefill_split_blocks(T, S, H, D)
+        return _lib.prefill_split_blocks(T, S, H, D, _DTYPES[dtype])
     if split is None:
         return 0
     if isinstance(split, bool) or not isinstance(split, int) or split < 1:
@@ -174,7 +174,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Ten
             0 if initial_state is None else initial_state.data_ptr(), d_out.data_ptr(),
             0 if d_final_state is None else d_final_state.data_ptr(), dq.data_ptr(),
             dk.data_ptr(), dv.data_ptr(), 0 if d_init is None else d_init.data_ptr())
-    seg_blocks = _seg_blocks(split, T, S, H, D)
+    seg_blocks = _seg_blocks(split, T, S, H, D, dtype)
     if seg_blocks > 0:
         nbytes = _lib.prefill_split_workspace_size(T, S, H, D, seg_blocks)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)

@@ -18,10 +18,12 @@ _PATH = os.path.join(_HERE, "liblightning_attn.so")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
+ABI_VERSION = 2  # LA_ABI_VERSION of include/lightning_attn.h
 
 # Every symbol declared in include/lightning_attn.h.
 EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_split",
-           "la_prefill_split_workspace_size", "la_prefill_split_blocks", "la_backward",
+           "la_prefill_split_workspace_size", "la_prefill_split_blocks",
+           "la_prefill_split_blocks_for", "la_backward",
            "la_backward_split",
            "la_decode_step", "la_decode_tokens",
            "la_status_str", "la_last_error")
@@ -61,6 +63,11 @@ def load():
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         lib.la_abi_version.argtypes = []
         lib.la_abi_version.restype = i32
+        if lib.la_abi_version() != ABI_VERSION:
+            raise RuntimeError(
+                "liblightning_attn.so at %s has ABI version %d, expected %d; rebuild it with "
+                "`python -m long_context_attention_attn_amd.build`"
+                % (_PATH, lib.la_abi_version(), ABI_VERSION))
         lib.la_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, ctypes.c_int, vp]
         lib.la_prefill.restype = ctypes.c_int
         lib.la_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
@@ -71,8 +78,10 @@ def load():
         lib.la_prefill_split.restype = ctypes.c_int
         lib.la_prefill_split_workspace_size.argtypes = [i64, i32, i32, i32, i32]
         lib.la_prefill_split_workspace_size.restype = ctypes.c_size_t
-        lib.la_prefill_split_blocks.argtypes = [i64, i32, i32, i32]
+        lib.la_prefill_split_blocks.argtypes = [i64, i32, i32, i32, ctypes.c_int]
         lib.la_prefill_split_blocks.restype = i32
+        lib.la_prefill_split_blocks_for.argtypes = [i64, i32, i32, i32, ctypes.c_int, i32]
+        lib.la_prefill_split_blocks_for.restype = i32
         lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32,
                                     i32, i32, ctypes.c_int, vp]
         lib.la_backward.restype = ctypes.c_int
@@ -125,8 +134,12 @@ def prefill_split_workspace_size(T, S, H, D, seg_blocks) -> int:
     return int(load().la_prefill_split_workspace_size(T, S, H, D, seg_blocks))
 
 
-def prefill_split_blocks(T, S, H, D) -> int:
-    return int(load().la_prefill_split_blocks(T, S, H, D))
+def prefill_split_blocks(T, S, H, D, dtype) -> int:
+    return int(load().la_prefill_split_blocks(T, S, H, D, dtype))
+
+
+def prefill_split_blocks_for(T, S, H, D, dtype, compute_units) -> int:
+    return int(load().la_prefill_split_blocks_for(T, S, H, D, dtype, compute_units))
 
 
 def backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state, dq, dk, dv,

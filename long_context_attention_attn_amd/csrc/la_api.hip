@@ -190,17 +190,34 @@ size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t 
   return split_layout(T, S, H, D, seg_blocks).bytes;
 }
 
-int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D) {
-  if (T <= 0 || S < 1 || H < 1 || (D != 64 && D != 128)) return 0;
+int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
+                                    int32_t compute_units) {
+  if (T <= 0 || S < 1 || H < 1 || (D != 64 && D != 128) || compute_units < 1) return 0;
+  if (dtype != LA_BF16 && dtype != LA_F32) return 0;
+  const int64_t slices = D / 32;
+  if ((int64_t)S * H * slices >= compute_units) return 0;  // the plain launch fills the device
+  const int64_t blocks = (T + 63) / 64;
+  int64_t seg = (blocks * H * slices + compute_units - 1) / compute_units;  // ~1 WG per CU
+  if (seg < 4) seg = 4;                               // keep segments a few blocks long
+  if (seg >= blocks || seg > 0x7fffffff) return 0;    // no sequence would be cut
+  // Cost model in microseconds, fitted to MI355X timings of both paths: one 64-token block
+  // step of a workgroup takes tb (bf16 0.75, fp32 4.5 at D = 128; 0.6x that at D = 64); the
+  // plain scan walks a sequence's blocks (the mean length T / S stands in for the longest); the
+  // split adds ~22 us of fixed cost (four launches), walks a segment twice (state-only pass and
+  // segment pass) and combines ~0.5 us per segment of a sequence serially.  Split only when it
+  // saves at least 10%.
+  const double tb = (dtype == LA_F32 ? 4.5 : 0.75) * (D == 64 ? 0.6 : 1.0);
+  const double nb = (double)((blocks + S - 1) / S);
+  const double plain = 8.0 + nb * tb;
+  const double split = 22.0 + 2.0 * (double)seg * tb + 0.5 * ((nb + seg - 1) / (double)seg);
+  if (split >= 0.9 * plain) return 0;
+  return (int32_t)seg;
+}
+
+int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype) {
   int cus = 0;
   if (check_device(&cus) != LA_OK || cus <= 0) return 0;
-  const int64_t slices = D / 32;
-  if ((int64_t)S * H * slices >= cus) return 0;  // the plain launch fills the device
-  const int64_t blocks = (T + 63) / 64;
-  int64_t seg = (blocks * H * slices + cus - 1) / cus;  // about one workgroup per CU
-  if (seg < 4) seg = 4;                                  // keep segments a few blocks long
-  if (seg >= blocks || seg > 0x7fffffff) return 0;       // no sequence would be cut
-  return (int32_t)seg;
+  return la_prefill_split_blocks_for(T, S, H, D, dtype, cus);
 }
 
 la_status la_prefill_split(const void *q, const void *k, const void *v, const float *decay,

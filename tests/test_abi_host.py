@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.la_abi_version() == 1
+    assert lib.la_abi_version() == 2
     assert lib.la_status_str(0) == b"LA_OK"
     assert lib.la_status_str(1) == b"LA_ERR_INVALID_ARG"
     assert lib.la_status_str(2) == b"LA_ERR_UNSUPPORTED"
@@ -151,7 +151,7 @@ def test_split_without_device(lib):
 
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
-    assert lib.la_prefill_split_blocks(8192, 1, 8, 128) == 0
+    assert lib.la_prefill_split_blocks(8192, 1, 8, 128, 1) == 0
     assert _split(lib) == 3
 
 
@@ -267,3 +267,39 @@ def test_backward_split_without_device(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert _backward_split(lib) == 3
+
+
+# Plain-vs-split choices measured on one MI355X (256 CUs), D = 128, one sequence: (dtype, H, T,
+# split faster by > 10%).  bf16: 512/1,024/2,048 tokens ran 11.5-29.5 us plain against
+# 24.4-31.3 us split; 4,096+ tokens split won (e.g. 8 heads: 51.9 -> 36.5 us).  fp32: 512 tokens
+# 39.4 us plain against 45.5 us split; 1,024+ split won (74.8 -> 49.1 us at 8 heads).
+SPLIT_MEASURED = [
+    (1, 1, 512, False), (1, 1, 1024, False), (1, 1, 4096, True), (1, 1, 16384, True),
+    (1, 8, 512, False), (1, 8, 1024, False), (1, 8, 2048, False), (1, 8, 4096, True),
+    (1, 8, 8192, True), (1, 16, 512, False), (1, 16, 2048, False), (1, 16, 8192, True),
+    (0, 1, 512, False), (0, 1, 1024, True), (0, 8, 512, False), (0, 8, 1024, True),
+    (0, 16, 2048, True), (0, 16, 16384, True),
+]
+
+
+@pytest.mark.parametrize("dtype,H,T,split", SPLIT_MEASURED)
+def test_split_suggestion_matches_measured_choice(lib, dtype, H, T, split):
+    seg = lib.la_prefill_split_blocks_for(T, 1, H, 128, dtype, 256)
+    assert (seg > 0) == split, (dtype, H, T, seg)
+
+
+def test_split_suggestion_rules(lib):
+    f = lib.la_prefill_split_blocks_for
+    # the plain launch already fills 256 CUs: 64 heads x 4 slices, or 2 x 32 heads
+    assert f(65536, 1, 64, 128, 1, 256) == 0
+    assert f(65536, 2, 32, 128, 1, 256) == 0
+    # few chains over a long sequence: about one segment workgroup per CU
+    assert f(65536, 1, 8, 128, 1, 256) == 128
+    assert f(65536, 1, 8, 64, 1, 256) == 64
+    # at least 4 blocks per segment, never a segment covering the whole sequence
+    assert f(16384, 1, 1, 128, 1, 256) == 4
+    assert f(256, 1, 1, 128, 1, 256) == 0
+    # invalid sizes, dtype or device size
+    for args in ((0, 1, 8, 128, 1, 256), (4096, 0, 8, 128, 1, 256), (4096, 1, 0, 128, 1, 256),
+                 (4096, 1, 8, 96, 1, 256), (4096, 1, 8, 128, 7, 256), (4096, 1, 8, 128, 1, 0)):
+        assert f(*args) == 0, args
