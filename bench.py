@@ -382,36 +382,52 @@ def copy_probe(mib, steps, warmup):
 
 
 def cpu_baseline(q, k, v, wl, n_tok, tokens_per_step):
-    """The fp64 oracle's recurrent form on the first n_tok tokens of the same input (all 64
-    heads), timed on the host; scaled to tokens/s of the 64-head workload."""
-    import oracle
+    """The fp64 oracle on the host cores for one step of the same workload: its recurrent form
+    (O2) on the first n_tok tokens of the prefill input (all 64 heads), scaled to the 65,536
+    tokens, plus its decode step (O4) on all 256 x 64 states of the decode shape (synthetic
+    values: the timing does not depend on them).  value = tokens per step / oracle seconds per
+    step, the GPU value's unit.  fp64 FLOP counted as 5 d^2 per token-head (decay, rank-1 update
+    and q S)."""
+    import torch
 
-    o = oracle.default()
-    qs = q[:n_tok].cpu()
-    ks = k[:n_tok].cpu()
-    vs = v[:n_tok].cpu()
-    decay = wl.decay()
-    # Convert outside the timed region (the oracle consumes fp64).
+    import oracle
+    from long_context_attention_attn_amd import synth
     from oracle import _f64  # noqa: PLC0415
 
-    qf, kf, vf = _f64(qs), _f64(ks), _f64(vs)
+    o = oracle.default()
+    decay = wl.decay()
+    dec64 = decay.double().numpy()
+    # Inputs converted outside the timed regions (the oracle consumes fp64).
+    qf, kf, vf = (_f64(x[:n_tok].cpu()) for x in (q, k, v))
+    qd, kd, vd = (_f64(x) for x in synth.decode_batch(BT_DECODE, H, D, torch.bfloat16, seed=2))
+    st = _f64(synth.random_state(BT_DECODE, H, D, seed=1, scale=0.1))
     threads = o.num_threads()
     t0 = time.perf_counter()
-    o.recurrent(qf, kf, vf, decay.double().numpy())
-    dt = time.perf_counter() - t0
-    # One thread on 4 heads of the same tokens (1/16 of the work), scaled to all 64 heads.
+    o.recurrent(qf, kf, vf, dec64)
+    dt_pre = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    o.decode_step(qd, kd, vd, dec64, st)
+    dt_dec = time.perf_counter() - t0
+    step_s = dt_pre * (T_PREFILL / n_tok) + dt_dec
+    flop_tok = 5 * D * D
+    # One thread on 4 heads of the same prefill tokens (1/16 of the work), scaled to 64 heads.
     heads1 = 4
     o.set_num_threads(1)
     t1 = time.perf_counter()
-    o.recurrent(qf[:, :heads1], kf[:, :heads1], vf[:, :heads1], decay[:heads1].double().numpy())
-    dt1 = (time.perf_counter() - t1) * (qf.shape[1] / heads1)
+    o.recurrent(qf[:, :heads1], kf[:, :heads1], vf[:, :heads1], dec64[:heads1])
+    dt1 = (time.perf_counter() - t1) * (H / heads1)
     o.set_num_threads(threads)
     return {
-        "value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-        "sample": "recurrent fp64 form on the first %d of 65536 tokens, all 64 heads "
-                  "(prefill only; %.1f s)" % (n_tok, dt),
-        "seconds": dt,
-        "single_thread": {"value": n_tok / dt1, "unit": "tokens/s", "cores": 1,
+        "value": tokens_per_step / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": "fp64 recurrent form on the first %d of %d prefill tokens (all %d heads, "
+                  "%.1f s, scaled to the full prefill) + fp64 decode step on %d x %d states "
+                  "(%.2f s)" % (n_tok, T_PREFILL, H, dt_pre, BT_DECODE, H, dt_dec),
+        "seconds_per_step": step_s,
+        "prefill_tokens_per_s": n_tok / dt_pre,
+        "prefill_fp64_gflops": n_tok * H * flop_tok / dt_pre / 1e9,
+        "decode_ms": dt_dec * 1e3,
+        "decode_fp64_gflops": BT_DECODE * H * flop_tok / dt_dec / 1e9,
+        "single_thread": {"value": n_tok / dt1, "unit": "prefill tokens/s", "cores": 1,
                           "sample": "same tokens, heads 0-3, scaled x16 to 64 heads"},
         "cpu_model": _cpu_model(),
     }
