@@ -286,7 +286,7 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   a.H = H;
   a.D = D;
   a.state_only = true;
-  e = prefill(a, s);
+  e = dtype == LA_BF16 ? la_launch_segment_states_bf16(a, (int64_t)seg_blocks * 64, s) : prefill(a, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "segment state launch: %s", hipGetErrorString(e));
   e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, final_state,
                         false, false, s);
@@ -472,7 +472,7 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
   a.H = H;
   a.D = D;
   a.state_only = true;
-  e = scan(a, s);
+  e = dtype == LA_BF16 ? la_launch_segment_states_bf16(a, (int64_t)seg_blocks * 64, s) : scan(a, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "dq segment states: %s", hipGetErrorString(e));
   e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, nullptr, true,
                         false, s);
@@ -500,7 +500,7 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
   b.D = D;
   b.reverse = true;
   b.state_only = true;
-  e = scan(b, s);
+  e = dtype == LA_BF16 ? la_launch_segment_states_bf16(b, (int64_t)seg_blocks * 64, s) : scan(b, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "dv/dk segment states: %s", hipGetErrorString(e));
   e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, d_final_state, states, d_initial_state,
                         false, true, s);

@@ -46,6 +46,13 @@ hipError_t la_launch_decode_multi_f32(const LaDecodeArgs &a, int32_t m, hipStrea
 hipError_t la_launch_seg_table(const int32_t *cu, int64_t T, int32_t S, int64_t seg_len,
                                int32_t cap, int32_t *seg_cu, int32_t *seq_seg0,
                                int32_t *seg_rfirst, hipStream_t stream);
+// Segment states of the split (bf16 storage): final_state[s][h] = the state a scan over
+// sequence s of (a.k, a.v) reaches from zero (a.reverse: scanning from its last token); uses
+// a.k, a.v, a.decay, a.cu_seqlens (required), a.final_state, a.S, a.H, a.D, a.reverse only
+// (a.state_only must be set: past its offset range it runs the prefill's state-only form).
+// max_len bounds every sequence's length.
+hipError_t la_launch_segment_states_bf16(const LaPrefillArgs &a, int64_t max_len,
+                                         hipStream_t stream);
 // s0_transposed: read s0[s][h][b][a] as element [a][b].  reverse_inclusive: walk each sequence's
 // segments from last to first (a reversed scan), the first one counting s0 as inclusive.
 hipError_t la_launch_combine(const float *decay, const int32_t *seg_cu, const int32_t *seq_seg0,

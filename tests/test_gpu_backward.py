@@ -173,7 +173,12 @@ def test_backward_split_ragged_varlen(dtype, D, with_states, seg_blocks):
 
 def test_backward_split_8k_recurrent():
     """8 heads x 8,192 tokens, D=128, bf16, 16-block segments (8 per sequence), with an initial
-    state and a final-state gradient: all heads against O7, and against the unsplit backward."""
+    state and a final-state gradient: all heads against O7, and against the unsplit backward.
+
+    The two paths round different bf16 operands (the split's segment states weight each token by
+    its power of lambda within the segment, the plain scan by its power within a 64-token block),
+    so they agree to bf16 rounding, not bit for bit: the fp32 d_initial_state of each is checked
+    against the oracle, and the split's error must stay within twice the plain one's."""
     wl = synth.workloads()["prefill_8k"]
     banner("backward split prefill_8k T=8192 H=8 D=128 bf16 seg_blocks=16")
     q, k, v = wl.inputs()
@@ -185,11 +190,14 @@ def test_backward_split_8k_recurrent():
     want = oracle.backward_recurrent(q, k, v, decay, do, init_state=init, d_final=dfs)
     _compare(got, want, [0, wl.T], BF16_TOL, "split 8k")
     plain = _gpu_backward(q, k, v, decay, do, None, init, dfs)
+    _compare(plain, want, [0, wl.T], BF16_TOL, "plain 8k")
     for name, a, b in zip(("dq", "dk", "dv"), got[:3], plain[:3]):
         e = slice_errors(to_np(a), to_np(b).astype(np.float64), [0, wl.T])
         assert float(e.max()) <= BF16_TOL, name
-    e = state_errors(to_np(got[3]), to_np(plain[3]).astype(np.float64))
-    assert float(e.max()) <= 1e-4
+    e_split = state_errors(to_np(got[3]), want[3]).max()
+    e_plain = state_errors(to_np(plain[3]), want[3]).max()
+    print("d_init vs oracle: split %.2e plain %.2e" % (e_split, e_plain))
+    assert e_split <= 2 * e_plain + 1e-5
 
 
 def test_autograd_split_matches_plain():
