@@ -11,7 +11,9 @@
   two-scan gradient form (the 64-head backward is in test_gpu_backward.py);
 * the fp32-storage path at length: 2 packed sequences of 40,003 and 25,590 tokens x 8 heads
   with initial states (prefill, plain and split), and the backward of 16,411 tokens x 4 heads
-  (plain and split), at the fp32 tolerance.
+  (plain and split), at the fp32 tolerance;
+* a split prefill of 1,200,000 tokens x 8 heads with 1,048,576-token segments (past the
+  offset range of the token-parallel segment states: the state-only scan runs instead).
 """
 import numpy as np
 import pytest
@@ -197,3 +199,23 @@ def test_backward_f32_16k():
             worst = max(worst, float(e.max()))
         print("fp32 backward split=%s: worst rel-L2 %.2e" % (split, worst), flush=True)
         assert worst <= F32_TOL, split
+
+
+def test_split_segments_past_offset_range():
+    """Split prefill whose longest segment (1,048,576 tokens x 8 heads x d128 bf16) is past the
+    32-bit offset range of the token-parallel segment states, so step 2 runs the block scan's
+    state-only form instead: heads {0, 7} against the recurrent form, outputs and final states."""
+    T, H, D, seg_blocks = 1_200_000, 8, 128, 16384
+    banner("split prefill T=%d H=%d D=%d bf16 seg_blocks=%d (segment-state fallback)"
+           % (T, H, D, seg_blocks))
+    q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=21, device="cuda")
+    decay = synth.decay_geometric(H, 0.9, 0.9999)
+    out, fs = la.prefill(q, k, v, decay.to(dev()), split=seg_blocks)
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    ref, ref_s = oracle.recurrent(_heads(q, heads), _heads(k, heads), _heads(v, heads),
+                                  decay[heads])
+    e = slice_errors(to_np(_heads(out, heads)), ref, [0, T])
+    es = state_errors(to_np(fs[:, heads]), ref_s)
+    print("split fallback: out %.2e state %.2e" % (e.max(), es.max()))
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
