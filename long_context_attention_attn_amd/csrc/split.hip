@@ -287,14 +287,18 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, base + voff[u], 0, 0));
   };
 
-  // Weights of this lane's V rows in the current chunk (fp64), and the per-step factor.
-  double wv[C::NVL];
+  // Weights of this lane's V rows in the current chunk (fp64), times wstep[u] after each step.
+  // A row past the end of the wave's first chunk (a partial last chunk of the segment; its data
+  // reads as zero there) starts at its weight in the wave's next chunk, lambda^(e+256), and
+  // skips the first step's factor.
+  double wv[C::NVL], wstep[C::NVL];
   const double lam256 = powd(lam, (int64_t)SS_CH * SS_WAVES);
   if (ch_hi >= 0) {
 #pragma unroll
     for (int u = 0; u < C::NVL; ++u) {
       const int64_t e = (int64_t)n - 1 - ((int64_t)ch_hi * SS_CH + 16 * u + vr);
-      wv[u] = e >= 0 ? powd(lam, e) : 0.0;
+      wv[u] = powd(lam, e >= 0 ? e : e + SS_CH * SS_WAVES);
+      wstep[u] = e >= 0 ? lam256 : 1.0;
     }
     fetch(ch_hi, kreg[0], vreg[0]);
     fetch(ch_hi - SS_WAVES >= 0 ? ch_hi - SS_WAVES : ch_hi, kreg[1], vreg[1]);
@@ -314,7 +318,8 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)vd[u][e] * ws);
       *(bf16x8 *)(vt + (16 * u + vr) * C::VPB + 16 * vp) = x;
-      wv[u] *= lam256;
+      wv[u] *= wstep[u];
+      wstep[u] = lam256;
     }
     // Unconditional (past the last chunk: this one again, never staged), so that the
     // outstanding-load count is the same on every path and a wait drains only the older set.

@@ -2,8 +2,10 @@
 the fp64 oracle, and against the plain prefill.
 
 Segment lengths of 1 and 2 blocks put segment boundaries inside every sequence of the ragged
-batch, next to empty sequences and partial last blocks; the 8k x 8 and 64k x 8 cases are the
-few-chain shapes the split exists for.
+batch, next to empty sequences and partial last blocks; segments of 9 and 16 blocks give every
+wave of the bf16 segment-state kernel several 32-token chunks (an odd and an even number, and a
+partial last chunk) at both head sizes, forward and reversed; the 8k x 8 and 64k x 8 cases are
+the few-chain shapes the split exists for.
 """
 import numpy as np
 import pytest
@@ -95,3 +97,39 @@ def test_split_64k_8_heads_recurrent():
     print("split 64k x 8: out", np.array2string(e[0], formatter={"float_kind": lambda x: "%.2e" % x}),
           "state max %.2e" % es.max())
     assert e.max() <= BF16_TOL and es.max() <= BF16_TOL
+
+
+LONG = [3001, 1, 2500, 0, 700, 1153]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("seg_blocks", [9, 16])
+def test_split_long_segments(D, seg_blocks):
+    """bf16, segments of 576 or 1,024 tokens over ragged sequences of 0..3,001 tokens (18 or 32
+    chunks per full segment: 2-4 per wave, partial last chunks), lambda = 0, 0.9, 0.999, 1 and an
+    initial state: the split prefill against O1 and O3, and the split backward (its reversed
+    segment states) against O7."""
+    banner("split long segments D=%d seg_blocks=%d" % (D, seg_blocks))
+    H = 4
+    cu = synth.cu_from_lengths(LONG)
+    T = int(cu[-1])
+    q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=60)
+    do, _, _ = synth.qkv(T, H, D, torch.bfloat16, seed=61)
+    decay = torch.tensor([0.0, 0.9, 0.999, 1.0], dtype=torch.float32)
+    init = synth.random_state(len(LONG), H, D, seed=62, scale=0.1)
+    dfs = synth.random_state(len(LONG), H, D, seed=63, scale=0.1)
+    out, fs = _split_prefill(q, k, v, decay, cu, init, split=seg_blocks)
+    ref = oracle.quadratic(q, k, v, decay, cu, init_state=init)
+    ref_s = oracle.final_state(k, v, decay, cu, init_state=init)
+    e = slice_errors(to_np(out), ref, cu)
+    es = state_errors(to_np(fs), ref_s)
+    d = dev()
+    g = la.backward(q.to(d), k.to(d), v.to(d), decay.to(d), do.to(d), cu.to(d),
+                    initial_state=init.to(d), d_final_state=dfs.to(d), split=seg_blocks)
+    torch.cuda.synchronize()
+    want = oracle.backward_recurrent(q, k, v, decay, do, cu, init_state=init, d_final=dfs)
+    eg = [float(slice_errors(to_np(x), w, cu).max()) for x, w in zip(g[:3], want[:3])]
+    eg.append(float(state_errors(to_np(g[3]), want[3]).max()))
+    print("split long: out %.2e state %.2e dq %.2e dk %.2e dv %.2e d_init %.2e"
+          % (e.max(), es.max(), *eg))
+    assert e.max() <= BF16_TOL and es.max() <= BF16_TOL and max(eg) <= BF16_TOL
