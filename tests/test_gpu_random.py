@@ -6,8 +6,10 @@ gradients, O4 decode).
 Each case draws 1-5 sequences of 0-700 tokens (some empty), 1-5 heads (head counts that are not
 multiples of 8 exercise the workgroup-mapping tail), d in {64, 128}, bf16 or fp32 storage,
 lambda per head in [0.5, 1] with exact 0 and 1 mixed in, an initial state and a final-state
-gradient or not, and a segment length of 1-3 blocks or no split.  Tolerances as everywhere:
-relative L2 per (sequence, head) slice <= 2e-2 (bf16) / 1e-4 (fp32)."""
+gradient or not, and a segment length of 1-3 blocks or no split.  Cases 48-63 draw 1-4
+sequences of 0-3,000 tokens with segments of 5, 9 or 16 blocks (or no split), so that the
+segment-state kernel's waves get several 32-token chunks, partial ones first.  Tolerances as
+everywhere: relative L2 per (sequence, head) slice <= 2e-2 (bf16) / 1e-4 (fp32)."""
 import numpy as np
 import pytest
 import torch
@@ -19,14 +21,16 @@ from long_context_attention_attn_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-CASES = 48
+CASES = 64
+LONG_FROM = 48  # cases from here on use long sequences and long segments
 TOL = {torch.bfloat16: BF16_TOL, torch.float32: F32_TOL}
 
 
 def _config(i):
     rng = np.random.default_rng(1000 + i)
-    S = int(rng.integers(1, 6))
-    lengths = [int(x) for x in rng.integers(0, 701, S)]
+    long = i >= LONG_FROM
+    S = int(rng.integers(1, 5 if long else 6))
+    lengths = [int(x) for x in rng.integers(0, 3001 if long else 701, S)]
     if rng.random() < 0.3:
         lengths[int(rng.integers(0, S))] = 0
     H = int(rng.integers(1, 6))
@@ -37,7 +41,10 @@ def _config(i):
         lam[int(rng.integers(0, H))] = 0.0
     if rng.random() < 0.4:
         lam[int(rng.integers(0, H))] = 1.0
-    split = int(rng.integers(1, 4)) if rng.random() < 0.5 else None
+    if long:
+        split = [None, 5, 9, 16][int(rng.integers(0, 4))]
+    else:
+        split = int(rng.integers(1, 4)) if rng.random() < 0.5 else None
     return dict(lengths=lengths, H=H, D=D, dtype=dtype, lam=lam, init=bool(rng.random() < 0.5),
                 dfs=bool(rng.random() < 0.5), split=split)
 
