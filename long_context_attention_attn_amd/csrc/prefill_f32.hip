@@ -39,7 +39,7 @@ constexpr int NTHR = 512;
 // Where a step stores the next block to LDS and issues the one after's loads: at d = 64 halfway
 // through the step (output waves after their scores, storing the previous block's outputs
 // there too; state waves between their two halves of products), at d = 128 at its end.
-// Measured side by side: halfway is 14% faster at d = 64 and 2-7% slower at d = 128.
+// Measured side by side: halfway is 12% faster at d = 64 and 2-7% slower at d = 128.
 template <int D>
 constexpr bool kMidStage = D == 64;
 
