@@ -36,12 +36,13 @@ namespace {
 constexpr int BLK = 64;
 constexpr int CV = 32;
 constexpr int NTHR = 512;
-// Where a step stores the next block to LDS and issues the one after's loads: at d = 64 halfway
-// through the step (output waves after their scores, storing the previous block's outputs
-// there too; state waves between their two halves of products), at d = 128 at its end.
-// Measured side by side: halfway is 12% faster at d = 64 and 2-7% slower at d = 128.
+// Where a step stores the next block to LDS and issues the one after's loads.  Output waves do
+// it halfway through the step (after their scores), together with the previous block's output
+// stores; state waves between their two halves of products at d = 64 and at the end of the step
+// at d = 128.  Measured side by side against doing both at the end: 12% faster at d = 64,
+// 4-5% faster at d = 128 (state waves halfway too there: 2-7% slower).
 template <int D>
-constexpr bool kMidStage = D == 64;
+constexpr bool kStateMidStage = D == 64;
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
@@ -156,7 +157,7 @@ struct Staged {
 // barrier.  The state waves publish the state after block i into the state copy 1-p.
 //
 // Output wave r: rows 16r..16r+15 of every block; its Q rows are loaded straight into
-// registers, one block ahead.
+// registers, one block ahead, and a block's outputs are stored halfway through the next step.
 template <int D, int R>
 __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) {
   constexpr int NT = R + 1;   // causal score tiles of the wave's rows
@@ -196,8 +197,7 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
     }
   const float isc_incl = sm.pw[jrow], isc_full = sm.pw[jrow + 1];
   float *const out_lane = x.out + x.row_off(jrow) + 4 * g;
-  constexpr bool MID = kMidStage<D>;
-  f32x4 o[2];             // with MID: the previous block's outputs, stored in the next step
+  f32x4 o[2];             // the previous block's outputs, stored in the next step
   float *odst = nullptr;  // where they go (null: nothing to store)
 
   int p = 0;
@@ -208,7 +208,7 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
     if (!x.so) {
       f32x4 qnext[NQ];
       load_q(qnext, i1 < x.n ? i1 : i0);
-      if constexpr (MID) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
       // sacc[t][i] = S^T[16t + 4g + i][jrow] = K[16t + 4g + i] . Q[jrow]
       f32x4 sacc[NT];
 #pragma unroll
@@ -221,16 +221,15 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
 #pragma unroll
           for (int m = 0; m < 4; ++m) sacc[t] = mfma4(kop[m], qop[qq][m], sacc[t]);
         }
-      if constexpr (MID) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (i1 < x.n) st.commit(sm, p ^ 1, tid);
-        if (odst) {
-          *(f32x4 *)odst = o[0];
-          *(f32x4 *)(odst + 16) = o[1];
-        }
-        st.fetch_or_last(x, i1 + BLK, ilast, tid);
-        __builtin_amdgcn_sched_barrier(0);
+      // Halfway: stage block i+1, store the previous block's outputs, issue block i+2's loads.
+      __builtin_amdgcn_sched_barrier(0);
+      if (i1 < x.n) st.commit(sm, p ^ 1, tid);
+      if (odst) {
+        *(f32x4 *)odst = o[0];
+        *(f32x4 *)(odst + 16) = o[1];
       }
+      st.fetch_or_last(x, i1 + BLK, ilast, tid);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -259,20 +258,10 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
 #pragma unroll
           for (int m = 0; m < 4; ++m)
             o[ct] = mfma4(sm.v[p][16 * t + 4 * g + m][16 * ct + c], sacc[t][m], o[ct]);
-      if constexpr (MID) {
-        odst = jrow < b ? out_lane + x.block_base(i0) : nullptr;
-      } else if (jrow < b) {
-        float *dst = out_lane + x.block_base(i0);
-        *(f32x4 *)dst = o[0];
-        *(f32x4 *)(dst + 16) = o[1];
-      }
+      odst = jrow < b ? out_lane + x.block_base(i0) : nullptr;
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) qop[qq] = qnext[qq];
-    } else if constexpr (MID) {
-      if (i1 < x.n) st.commit(sm, p ^ 1, tid);
-      st.fetch_or_last(x, i1 + BLK, ilast, tid);
-    }
-    if constexpr (!MID) {
+    } else {
       if (i1 < x.n) st.commit(sm, p ^ 1, tid);
       st.fetch_or_last(x, i1 + BLK, ilast, tid);
     }
@@ -292,7 +281,7 @@ __device__ __forceinline__ void state_wave(const Ctx &x, Smem<D> &sm, const floa
   using TL = Tiles<D>;
   constexpr int NTL = TL::count(R);
   constexpr int T0 = TL::first(R);
-  constexpr bool MID = kMidStage<D>;
+  constexpr bool MID = kStateMidStage<D>;
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int64_t ilast = x.n > 0 ? (x.n - 1) / BLK * BLK : 0;
 
