@@ -37,10 +37,10 @@ constexpr int BLK = 64;
 constexpr int CV = 32;
 constexpr int NTHR = 512;
 // Where a step stores the next block to LDS and issues the one after's loads.  Output waves do
-// it halfway through the step (after their scores), together with the previous block's output
+// it between their inter and intra products, together with the previous block's output
 // stores; state waves between their two halves of products at d = 64 and at the end of the step
-// at d = 128.  Measured side by side against doing both at the end: 12% faster at d = 64,
-// 4-5% faster at d = 128 (state waves halfway too there: 2-7% slower).
+// at d = 128.  Measured side by side against doing both at the end of the step: 13% faster at
+// d = 64, 6% faster at d = 128 (state waves halfway too there: 2-7% slower).
 template <int D>
 constexpr bool kStateMidStage = D == 64;
 
@@ -157,7 +157,8 @@ struct Staged {
 // barrier.  The state waves publish the state after block i into the state copy 1-p.
 //
 // Output wave r: rows 16r..16r+15 of every block; its Q rows are loaded straight into
-// registers, one block ahead, and a block's outputs are stored halfway through the next step.
+// registers, one block ahead, and a block's outputs are stored in the next step, between its
+// inter and intra products.
 template <int D, int R>
 __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) {
   constexpr int NT = R + 1;   // causal score tiles of the wave's rows
@@ -197,7 +198,7 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
     }
   const float isc_incl = sm.pw[jrow], isc_full = sm.pw[jrow + 1];
   float *const out_lane = x.out + x.row_off(jrow) + 4 * g;
-  f32x4 o[2];             // the previous block's outputs, stored in the next step
+  f32x4 o[2] = {};        // the previous block's outputs, stored in the next step
   float *odst = nullptr;  // where they go (null: nothing to store)
 
   int p = 0;
@@ -221,15 +222,6 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
 #pragma unroll
           for (int m = 0; m < 4; ++m) sacc[t] = mfma4(kop[m], qop[qq][m], sacc[t]);
         }
-      // Halfway: stage block i+1, store the previous block's outputs, issue block i+2's loads.
-      __builtin_amdgcn_sched_barrier(0);
-      if (i1 < x.n) st.commit(sm, p ^ 1, tid);
-      if (odst) {
-        *(f32x4 *)odst = o[0];
-        *(f32x4 *)(odst + 16) = o[1];
-      }
-      st.fetch_or_last(x, i1 + BLK, ilast, tid);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -238,6 +230,7 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
           sacc[t][i] = key <= jrow ? sacc[t][i] * mw[t][i] : 0.f;
         }
       // Inter part: o[ct][i] = sum_a KV[a][c0 + 16ct + 4g + i] Q[jrow][a].
+      const f32x4 op0 = o[0], op1 = o[1];  // previous block's outputs
       o[0] = o[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq)
@@ -247,6 +240,16 @@ __device__ __forceinline__ void output_wave(const Ctx &x, Smem<D> &sm, int tid) 
 #pragma unroll
           for (int m = 0; m < 4; ++m) o[ct] = mfma4(kvo[m], qop[qq][m], o[ct]);
         }
+      // Between the inter and intra products: stage block i+1, store the previous block's
+      // outputs, issue block i+2's loads.
+      __builtin_amdgcn_sched_barrier(0);
+      if (i1 < x.n) st.commit(sm, p ^ 1, tid);
+      if (odst) {
+        *(f32x4 *)odst = op0;
+        *(f32x4 *)(odst + 16) = op1;
+      }
+      st.fetch_or_last(x, i1 + BLK, ilast, tid);
+      __builtin_amdgcn_sched_barrier(0);
       const float isc = i0 == 0 && x.incl ? isc_incl : isc_full;
       o[0] *= isc;
       o[1] *= isc;
