@@ -133,3 +133,23 @@ def test_split_long_segments(D, seg_blocks):
     print("split long: out %.2e state %.2e dq %.2e dk %.2e dv %.2e d_init %.2e"
           % (e.max(), es.max(), *eg))
     assert e.max() <= BF16_TOL and es.max() <= BF16_TOL and max(eg) <= BF16_TOL
+
+
+def test_split_suggestion_uses_the_device():
+    """la_prefill_split_blocks on the device equals the pure rule at the device's CU count, and
+    split="auto" runs the suggested segment length (same outputs as that explicit split)."""
+    from long_context_attention_attn_amd import _lib
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for T, S, H, D, dt in ((65536, 1, 8, 128, 1), (4096, 1, 8, 128, 1), (1024, 1, 8, 128, 0),
+                           (512, 1, 1, 64, 1), (65536, 1, 64, 128, 1), (200000, 4, 4, 64, 0)):
+        assert (_lib.prefill_split_blocks(T, S, H, D, dt)
+                == _lib.prefill_split_blocks_for(T, S, H, D, dt, cus)), (T, S, H, D, dt)
+    T, H, D = 8192, 8, 128
+    seg = _lib.prefill_split_blocks(T, 1, H, D, _lib.LA_BF16)
+    assert seg > 0
+    q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=70)
+    decay = synth.decay_geometric(H, 0.9, 0.9999)
+    oa, fa = _split_prefill(q, k, v, decay, split="auto")
+    ob, fb = _split_prefill(q, k, v, decay, split=seg)
+    assert torch.equal(oa, ob) and torch.equal(fa, fb)
