@@ -121,6 +121,37 @@ SplitLayout split_layout(int64_t T, int32_t S, int32_t H, int32_t D, int32_t seg
   return l;
 }
 
+
+// Piecewise-linear cost (microseconds) of one 64-token block step of a workgroup, as a function
+// of how many workgroups run at once (first column).  bf16 has two tables: inputs that stay in
+// the 256 MB last-level cache between passes, and inputs that stream from HBM.
+struct CostPt { double w, us; };
+constexpr CostPt kBf16D128Cached[] = {{1, 0.71}, {32, 0.70}, {128, 0.75}, {256, 0.87}};
+constexpr CostPt kBf16D128Hbm[] = {{1, 0.71}, {32, 0.865}, {128, 0.92}, {256, 1.06}};
+constexpr CostPt kBf16D64Cached[] = {{1, 0.51}, {16, 0.61}, {64, 0.63}, {128, 0.64}, {256, 0.66}};
+constexpr CostPt kBf16D64Hbm[] = {{1, 0.51}, {16, 0.625}, {64, 1.06}, {128, 1.11}, {256, 1.10}};
+
+double cost_at(const CostPt *t, int n, double w) {
+  if (w <= t[0].w) return t[0].us;
+  for (int i = 1; i < n; ++i)
+    if (w <= t[i].w) return t[i - 1].us + (t[i].us - t[i - 1].us) * (w - t[i - 1].w) /
+                                             (t[i].w - t[i - 1].w);
+  return t[n - 1].us;
+}
+#define LA_COST_AT(table, w) cost_at(table, (int)(sizeof(table) / sizeof(table[0])), w)
+
+// Block-step cost for `w` concurrent workgroups over `bytes` of q, k, v and out.  fp32 is bound
+// by its matrix products and costs the same at any load; bf16 blends its cached and streaming
+// tables as the working set grows from 256 MiB to 512 MiB.
+double block_cost(la_dtype dtype, int32_t D, double w, double bytes) {
+  if (dtype == LA_F32) return D == 64 ? 2.7 : 4.4;
+  const double mib = 1024.0 * 1024.0;
+  double f = (bytes - 256 * mib) / (256 * mib);
+  f = f < 0 ? 0 : (f > 1 ? 1 : f);
+  const double c = D == 64 ? LA_COST_AT(kBf16D64Cached, w) : LA_COST_AT(kBf16D128Cached, w);
+  const double h = D == 64 ? LA_COST_AT(kBf16D64Hbm, w) : LA_COST_AT(kBf16D128Hbm, w);
+  return (1 - f) * c + f * h;
+}
 }  // namespace
 
 extern "C" {
@@ -200,17 +231,23 @@ int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, 
   int64_t seg = (blocks * H * slices + compute_units - 1) / compute_units;  // ~1 WG per CU
   if (seg < 4) seg = 4;                               // keep segments a few blocks long
   if (seg >= blocks || seg > 0x7fffffff) return 0;    // no sequence would be cut
-  // Cost model in microseconds, fitted to MI355X timings of both paths: one 64-token block
-  // step of a workgroup takes tb (bf16 0.75, fp32 4.5 at D = 128; 0.6x that at D = 64); the
-  // plain scan walks a sequence's blocks (the mean length T / S stands in for the longest); the
-  // split adds ~22 us of fixed cost (four launches), walks a segment twice (state-only pass and
-  // segment pass) and combines ~0.5 us per segment of a sequence serially.  Split only when it
-  // saves at least 10%.
-  const double tb = (dtype == LA_F32 ? 4.5 : 0.75) * (D == 64 ? 0.6 : 1.0);
-  const double nb = (double)((blocks + S - 1) / S);
-  const double plain = 8.0 + nb * tb;
-  const double split = 22.0 + 2.0 * (double)seg * tb + 0.5 * ((nb + seg - 1) / (double)seg);
-  if (split >= 0.9 * plain) return 0;
+  // Cost model in microseconds, fitted to MI355X timings of both paths over T = 512 .. 65,536,
+  // H = 1 .. 64, both head sizes and both dtypes.  The plain scan is ~6 us of launch plus one
+  // block step per block of a sequence (the mean length T / S stands in for the longest) with
+  // S * H * slices workgroups in flight.  The split is ~17 us of launches, the segment pass (one
+  // block step per block of a segment, the device full), the segment-state pass (0.55 of that
+  // for bf16, whose state pass runs token-parallel; 0.75 for fp32) and ~0.5 us per segment of a
+  // sequence in the serial combine.  Split only when it saves at least 5%.
+  const double bytes = (double)T * H * D * elem_bytes(dtype) * 4.0;
+  const int64_t nb = (blocks + S - 1) / S;                // blocks of a (mean) sequence
+  const double w_plain = (double)S * H * slices;
+  double w_split = (double)((blocks + seg - 1) / seg + S - 1) * H * slices;  // all segments
+  if (w_split > compute_units) w_split = compute_units;
+  const double plain = 6.0 + (double)nb * block_cost(dtype, D, w_plain, bytes);
+  const double so = dtype == LA_F32 ? 0.75 : 0.55;
+  const double split = 17.0 + (double)seg * block_cost(dtype, D, w_split, bytes) * (1.0 + so) +
+                       0.5 * (double)((nb + seg - 1) / seg);
+  if (split >= 0.95 * plain) return 0;
   return (int32_t)seg;
 }
 

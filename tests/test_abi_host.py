@@ -269,23 +269,60 @@ def test_backward_split_without_device(lib):
     assert _backward_split(lib) == 3
 
 
-# Plain-vs-split choices measured on one MI355X (256 CUs), D = 128, one sequence: (dtype, H, T,
-# split faster by > 10%).  bf16: 512/1,024/2,048 tokens ran 11.5-29.5 us plain against
-# 24.4-31.3 us split; 4,096+ tokens split won (e.g. 8 heads: 51.9 -> 36.5 us).  fp32: 512 tokens
-# 39.4 us plain against 45.5 us split; 1,024+ split won (74.8 -> 49.1 us at 8 heads).
+# Plain-vs-split choices timed on one MI355X (256 CUs), 20 calls of each path after warm-up,
+# one sequence, the suggested segment length: (dtype, D, H, T, split wins).  Only cases where one
+# path beat the other by 10% or more are pins; closer ones may go either way.  Examples, plain
+# against split in us: bf16 D = 128 H = 1: T = 1024 17.8 / 23.7, T = 2048 29.4 / 25.5; H = 32
+# T = 65536 945 / 857.  bf16 D = 64: H = 64 T = 65536 1147 / 899; H = 32 T = 2048 22.4 / 26.9.
+# fp32 D = 128: H = 1 T = 1024 73.8 / 47.2; H = 32 T = 16384 1128 / 967.  fp32 D = 64: H = 64
+# T = 1024 48.8 / 56.4.
 SPLIT_MEASURED = [
-    (1, 1, 512, False), (1, 1, 1024, False), (1, 1, 4096, True), (1, 1, 16384, True),
-    (1, 8, 512, False), (1, 8, 1024, False), (1, 8, 2048, False), (1, 8, 4096, True),
-    (1, 8, 8192, True), (1, 16, 512, False), (1, 16, 2048, False), (1, 16, 8192, True),
-    (0, 1, 512, False), (0, 1, 1024, True), (0, 8, 512, False), (0, 8, 1024, True),
-    (0, 16, 2048, True), (0, 16, 16384, True),
+    (1, 128, 1, 512, False), (1, 128, 1, 1024, False), (1, 128, 1, 2048, True),
+    (1, 128, 1, 4096, True), (1, 128, 1, 16384, True), (1, 128, 1, 65536, True),
+    (1, 128, 8, 512, False), (1, 128, 8, 1024, False), (1, 128, 8, 4096, True),
+    (1, 128, 8, 16384, True), (1, 128, 8, 65536, True), (1, 128, 32, 512, False),
+    (1, 128, 32, 1024, False), (1, 128, 32, 2048, False), (1, 128, 32, 65536, True),
+    (1, 64, 1, 512, False), (1, 64, 1, 1024, False), (1, 64, 1, 4096, True),
+    (1, 64, 1, 16384, True), (1, 64, 1, 65536, True), (1, 64, 8, 512, False),
+    (1, 64, 8, 1024, False), (1, 64, 8, 4096, True), (1, 64, 8, 16384, True),
+    (1, 64, 8, 65536, True), (1, 64, 32, 512, False), (1, 64, 32, 1024, False),
+    (1, 64, 32, 2048, False), (1, 64, 32, 4096, True), (1, 64, 32, 16384, True),
+    (1, 64, 32, 65536, True), (1, 64, 64, 512, False), (1, 64, 64, 1024, False),
+    (1, 64, 64, 2048, False), (1, 64, 64, 16384, True), (1, 64, 64, 65536, True),
+    (0, 128, 1, 512, False), (0, 128, 1, 1024, True), (0, 128, 1, 2048, True),
+    (0, 128, 1, 4096, True), (0, 128, 1, 16384, True), (0, 128, 1, 65536, True),
+    (0, 128, 8, 512, False), (0, 128, 8, 1024, True), (0, 128, 8, 2048, True),
+    (0, 128, 8, 4096, True), (0, 128, 8, 16384, True), (0, 128, 8, 65536, True),
+    (0, 128, 32, 512, False), (0, 128, 32, 16384, True), (0, 64, 1, 512, False),
+    (0, 64, 1, 1024, True), (0, 64, 1, 2048, True), (0, 64, 1, 4096, True),
+    (0, 64, 1, 16384, True), (0, 64, 1, 65536, True), (0, 64, 8, 512, False),
+    (0, 64, 8, 1024, True), (0, 64, 8, 2048, True), (0, 64, 8, 4096, True),
+    (0, 64, 8, 16384, True), (0, 64, 8, 65536, True), (0, 64, 32, 512, False),
+    (0, 64, 32, 1024, True), (0, 64, 32, 2048, True), (0, 64, 32, 4096, True),
+    (0, 64, 32, 16384, True), (0, 64, 64, 512, False), (0, 64, 64, 1024, False),
 ]
 
 
-@pytest.mark.parametrize("dtype,H,T,split", SPLIT_MEASURED)
-def test_split_suggestion_matches_measured_choice(lib, dtype, H, T, split):
-    seg = lib.la_prefill_split_blocks_for(T, 1, H, 128, dtype, 256)
-    assert (seg > 0) == split, (dtype, H, T, seg)
+# Several sequences (S equal lengths of T / S tokens), timed the same way: (dtype, D, H, S, T,
+# split wins).  fp32 D = 64 one head, 8 x 1,024 tokens: plain 47.0 us / split 35.5; fp32
+# D = 128 74.3 / 48.7; bf16 D = 128 17.9 / 25.1; bf16 D = 64 13.8 / 22.4; bf16 D = 64
+# H = 4, 4 x 8,192: 76.6 / 41.1; fp32 D = 128 H = 8, 2 x 32,768: 2234 / 971.
+SPLIT_MEASURED_BATCHED = [
+    (0, 64, 1, 8, 8192, True), (0, 128, 1, 8, 8192, True), (1, 128, 1, 8, 8192, False),
+    (1, 64, 1, 8, 8192, False), (1, 64, 4, 4, 32768, True), (0, 128, 8, 2, 65536, True),
+]
+
+
+@pytest.mark.parametrize("dtype,D,H,T,split", SPLIT_MEASURED)
+def test_split_suggestion_matches_measured_choice(lib, dtype, D, H, T, split):
+    seg = lib.la_prefill_split_blocks_for(T, 1, H, D, dtype, 256)
+    assert (seg > 0) == split, (dtype, D, H, T, seg)
+
+
+@pytest.mark.parametrize("dtype,D,H,S,T,split", SPLIT_MEASURED_BATCHED)
+def test_split_suggestion_matches_measured_choice_batched(lib, dtype, D, H, S, T, split):
+    seg = lib.la_prefill_split_blocks_for(T, S, H, D, dtype, 256)
+    assert (seg > 0) == split, (dtype, D, H, S, T, seg)
 
 
 def test_split_suggestion_rules(lib):
