@@ -408,15 +408,19 @@ __device__ __forceinline__ void dma_rows(const char *base, const Span &s, const 
   }
 }
 
-// L2 prefetch of block rows 16s..16s+15 (s = this workgroup's value slice) of q, k and the full
-// v rows, two blocks before their DMA (farther ahead, the 4 MB L2 of an XCD evicts prefetched
-// lines before their use, measured): one 16-byte read per 128-byte line, written to a
-// scratch area of LDS that nothing reads.  The D/32 slices of a head together cover all 64 rows
-// once, and the later DMAs of all four slices then hit L2 instead of waiting on HBM.
+// L2 prefetch of a share of the block's rows of q, k and the full v rows, two blocks before
+// their DMA (farther ahead, the 4 MB L2 of an XCD evicts prefetched lines before their use,
+// measured): one 16-byte read per 128-byte line, written to a scratch area of LDS that nothing
+// reads.  Slice s takes rows (64 / (D/32)) s onwards: 16 rows of two lines at D = 128 (four
+// slices), 32 rows of one line at D = 64 (two slices; lanes 32..63 repeat lanes 0..31), so the
+// slices of a head together cover all 64 rows once and the later DMAs of every slice hit L2
+// instead of waiting on HBM.
 template <int D, bool REV>
 __device__ __forceinline__ uint32_t prefetch_offset(int slice, int lane, uint32_t rowbytes) {
-  return lane_base<REV>(16 * slice + ((lane >> 1) & 15), (uint32_t)(lane & 1) * (D == 128 ? 128u : 64u),
-                        rowbytes);
+  if constexpr (D == 128)
+    return lane_base<REV>(16 * slice + ((lane >> 1) & 15), (uint32_t)(lane & 1) * 128u, rowbytes);
+  else
+    return lane_base<REV>(32 * slice + (lane & 31), 0u, rowbytes);
 }
 template <bool SO, bool REV>
 __device__ __forceinline__ void prefetch_l2(const Chain &c, const Span &s, uint32_t off,

@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times:
 
 * 64 heads x 65,536 tokens (one MiniMax-like layer): every output and state of all heads
-  against the oracle's recurrent form, plus sampled rows against the quadratic form;
+  against the oracle's recurrent form, plus block-edge rows and 32 random rows of every head
+  (256 random rows of heads {0, 21, 42, 63}) against the quadratic (definition) form;
 * 16 packed sequences of 1,024..32,768 tokens x 64 heads: every output and state of every
   (sequence, head) pair against the recurrent form;
 * 1,048,576 tokens x 64 heads (int64 indexing: T*H*D > 2^31): heads {0, 21, 42, 63} against
@@ -49,15 +50,21 @@ def test_prefill_64k_all_heads():
         es = state_errors(to_np(fs[:, hs]), ref_s)
         worst, worst_s = max(worst, e.max()), max(worst_s, es.max())
         print("heads %d..%d: out %.2e state %.2e" % (h0, h0 + 15, e.max(), es.max()), flush=True)
-    # Sampled rows against the quadratic (definition) form on all heads.
+    # Sampled rows against the quadratic (definition) form: block edges and 32 random rows on
+    # every head, 256 random rows on heads spanning the decay range.
     rng = np.random.default_rng(0)
-    rows = sorted(set([0, 1, 63, 64, 65, 4095, 4096, wl.T - 1] +
-                      [int(x) for x in rng.integers(0, wl.T, 24)]))
+    edges = [0, 1, 63, 64, 65, 127, 128, 129, 4095, 4096, 4097, wl.T - 65, wl.T - 64, wl.T - 2,
+             wl.T - 1]
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
-    refr = oracle.quadratic_rows(qc, kc, vc, decay, rows)
-    got = to_np(out[rows])
-    for h in range(wl.H):
-        assert rel(got[:, h], refr[:, h]) <= BF16_TOL, "row sample head %d" % h
+    for hs, n_rand in ((list(range(wl.H)), 32), (SAMPLED_HEADS, 256)):
+        rows = sorted(set(edges + [int(x) for x in rng.integers(0, wl.T, n_rand)]))
+        refr = oracle.quadratic_rows(qc[:, hs].contiguous(), kc[:, hs].contiguous(),
+                                     vc[:, hs].contiguous(), decay[hs], rows)
+        got = to_np(out[rows][:, hs])
+        for i, h in enumerate(hs):
+            assert rel(got[:, i], refr[:, i]) <= BF16_TOL, "row sample head %d" % h
+        print("%d rows x %d heads against the quadratic form: ok" % (len(rows), len(hs)),
+              flush=True)
     print("prefill_64k: worst out %.2e worst state %.2e" % (worst, worst_s))
     assert worst <= BF16_TOL and worst_s <= BF16_TOL
 
