@@ -129,7 +129,7 @@ struct CostPt { double w, us; };
 constexpr CostPt kBf16D128Cached[] = {{1, 0.71}, {32, 0.70}, {128, 0.75}, {256, 0.87}};
 constexpr CostPt kBf16D128Hbm[] = {{1, 0.71}, {32, 0.865}, {128, 0.92}, {256, 1.06}};
 constexpr CostPt kBf16D64Cached[] = {{1, 0.51}, {16, 0.61}, {64, 0.63}, {128, 0.64}, {256, 0.66}};
-constexpr CostPt kBf16D64Hbm[] = {{1, 0.51}, {16, 0.625}, {64, 1.06}, {128, 1.11}, {256, 1.10}};
+constexpr CostPt kBf16D64Hbm[] = {{1, 0.51}, {16, 0.60}, {64, 0.87}, {128, 0.91}, {256, 0.97}};
 
 double cost_at(const CostPt *t, int n, double w) {
   if (w <= t[0].w) return t[0].us;
