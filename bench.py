@@ -9,11 +9,14 @@ Inputs are resident in HBM before the timed region.  The timed region holds exac
 bracketed by device synchronisation; per-kernel durations come from HIP events recorded on
 the stream the kernels run on.
 
-Prints ONE JSON line with the roofline of the dominant kernel (prefill) and the fp64 CPU
-oracle timed on a bounded sample of the same workload (--no-cpu-baseline skips it).  Extra
-legs, timed after the K steps (--no-extras skips them): few-chain prefill and backward, plain
-and sequence-split; the 64-head backward; multi-token decode; the fp32-storage prefill; and
-ceilings re-measured on the device (copy bandwidth, library GEMM rates).
+`value` is prefill tokens/s (65,536 tokens over the prefill's own time from HIP events); the
+whole step's rate is step_tokens_per_s.  Prints ONE JSON line with the roofline of the dominant
+kernel (prefill: achieved from this run's HIP events, and the committed rocprofv3 trace's
+figure beside it) and the fp64 CPU oracle timed on a bounded sample of the same workload
+(--no-cpu-baseline skips it).  Extra legs, timed after the K steps (--no-extras skips them):
+the packed 16-sequence and the 1,048,576-token prefills at 64 heads; few-chain prefill and
+backward, plain and sequence-split; the 64-head backward; multi-token decode; the fp32-storage
+prefill; and ceilings re-measured on the device (copy bandwidth, library GEMM rates).
 """
 from __future__ import annotations
 
@@ -120,7 +123,10 @@ def main():
     ms_per_step = wall * 1e3 / K
 
     tokens_per_step = T_PREFILL + BT_DECODE
-    value = tokens_per_step / (ms_per_step / 1e3)
+    # The metric is prefill tokens/s: prefill tokens over the prefill kernel's own time (HIP
+    # events on its stream).  The whole step's rate (prefill and decode tokens over the step's
+    # wall time) is reported beside it as step_tokens_per_s.
+    value = T_PREFILL / (pre_avg / 1e3)
     pf = prefill_flop(T_PREFILL, H, D)
     pb = prefill_bytes(T_PREFILL, H, D)
     db = decode_bytes(BT_DECODE, H, D)
@@ -136,6 +142,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_tokens_per_s": tokens_per_step / (ms_per_step / 1e3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -163,11 +170,15 @@ def main():
             "bound": "hbm", "kernel": "prefill_bf16_kernel<128, false, false>",
             "achieved": pre_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": pre_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
+            "achieved_source": "HIP events around the prefill launches of this run",
+            "trace": committed_trace(pb),
         },
     }
 
     if not args.no_extras:
         del q, k, v, out
+        result["varlen_prefill"] = long_prefill_leg("varlen_16", dev)
+        result["long_prefill"] = long_prefill_leg("prefill_1m", dev)
         result["few_chain_prefill"] = few_chain_prefill(dev)
         result["backward"] = backward_leg(wl, dev)
         result["few_chain_backward"] = few_chain_backward(dev)
@@ -297,6 +308,55 @@ def few_chain_backward(dev, iters=10, warmup=2):
     return {"tokens": T, "heads": Hc, "seg_blocks": seg, "plain_ms": plain, "split_ms": split,
             "speedup": plain / split, "split_algorithmic_GBps": nbytes / (split / 1e3) / 1e9,
             "split_tokens_per_s": T / (split / 1e3)}
+
+
+def long_prefill_leg(name, dev, iters=5, warmup=2):
+    """The other full-size prefill workloads at 64 heads x d128 bf16, timed with HIP events:
+    16 packed sequences of 1,024-32,768 tokens (T = 272,568, state reset at every boundary) and
+    one 1,048,576-token sequence.  Tokens/s, TFLOP/s at B = 64 accounting and algorithmic
+    HBM GB/s against the 8 TB/s peak."""
+    import torch
+
+    import long_context_attention_attn_amd as la
+    from long_context_attention_attn_amd import synth
+
+    wl = synth.workloads()[name]
+    q, k, v = wl.inputs(device=dev)
+    decay = wl.decay().to(dev)
+    cu = wl.cu_seqlens().to(dev) if wl.S > 1 else None
+    out = torch.empty_like(q)
+    fs = torch.empty((wl.S, wl.H, wl.D, wl.D), dtype=torch.float32, device=dev)
+    ms = time_ms(lambda: la.prefill(q, k, v, decay, cu, out=out, final_state=fs), iters, warmup)
+    del q, k, v, out, fs
+    torch.cuda.empty_cache()
+    nbytes = prefill_bytes(wl.T, wl.H, wl.D, wl.S)
+    flop = prefill_flop(wl.T, wl.H, wl.D)
+    gbps = nbytes / (ms / 1e3) / 1e9
+    return {"workload": wl.note, "tokens": wl.T, "sequences": wl.S, "heads": wl.H, "ms": ms,
+            "tokens_per_s": wl.T / (ms / 1e3), "tflops": flop / (ms / 1e3) / 1e12,
+            "pct_bf16_mfma_peak": 100.0 * flop / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+            "algorithmic_bytes": nbytes, "algorithmic_GBps": gbps,
+            "hbm_frac": gbps / HBM_PEAK_GBPS}
+
+
+def committed_trace(nbytes):
+    """The prefill kernel's average duration in the committed rocprofv3 kernel trace
+    (profiles/prefill_kernel_trace.json) with the fraction of the HBM roofline it gives and the
+    shader clock the counter run measured; None when the kernel source changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "prefill_kernel_trace.json")
+    try:
+        doc = json.load(open(path))
+        src = open(os.path.join(ROOT, doc["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != doc.get("kernel_source_sha256"):
+        return None
+    us = doc["avg_us"]
+    gbps = nbytes / (us / 1e6) / 1e9
+    return {"source": doc.get("summary"), "avg_us": us, "achieved": gbps,
+            "frac": gbps / HBM_PEAK_GBPS, "shader_clock_mhz": doc.get("shader_clock_mhz")}
 
 
 def measured_traffic():

@@ -31,9 +31,20 @@
  * (fp32 storage and arithmetic).  Devices: gfx950 only.
  *
  * Ownership and memory.  The caller owns every buffer; the library keeps no pointer after a
- * call returns and allocates no device memory.  out must not overlap q, k or v; state buffers
- * must not overlap each other or the activations.  The host checks these byte ranges (from the
- * sizes given) and returns LA_ERR_INVALID_ARG on an overlap; q, k and v may share memory.
+ * call returns and allocates no device memory.  Every buffer a call writes (out, the states it
+ * writes or updates, gradients, a workspace) must not overlap any other buffer argument of the
+ * call, read or written, decay and cu_seqlens included; buffers that are only read (q, k, v,
+ * decay, an initial state, ...) may share memory.  The host checks these byte ranges (from the
+ * sizes given) and returns LA_ERR_INVALID_ARG on an overlap.
+ *
+ * Finite inputs.  q, k, v (and states) must be finite.  The definition masks future tokens out
+ * by selection, so a non-finite value could never reach an earlier output; the kernels keep
+ * that for q and k (future scores are selected away, the state only carries a token forward),
+ * but a block's matrix products multiply the masked-out (exactly zero) weights by v on the
+ * matrix cores, and 0 * inf or 0 * NaN is NaN there.  So a non-finite v at token t reaches
+ * earlier outputs of its own 64-token block (within the 32-token operand group of the intra
+ * product in bf16, the 16-token tile in fp32), never those of an earlier block nor anything
+ * before the sequence's start.
  *
  * Errors.  Argument checks run on the host before any HIP call and return a status; nothing
  * throws across this ABI.  Device data is not validated: non-monotone cu_seqlens or lambda
@@ -66,7 +77,10 @@ typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 int32_t la_abi_version(void);
 
 /*
- * Prefill (the block-wise forward pass).
+ * Prefill (the block-wise forward pass): within each 64-token block the left product, across
+ * blocks the right product through the running state (digest, section 1), over a packed batch
+ * of sequences delimited by cu_seqlens with the state reset at every sequence start (digest,
+ * section 4, data packing).
  *   q, k, v     in  [T][H][D] dtype           (may be NULL when T == 0)
  *   decay       in  [H] float32
  *   cu_seqlens  in  [S+1] int32, or NULL meaning one sequence of length T (then S must be 1)
@@ -81,8 +95,11 @@ la_status la_prefill(const void *q, const void *k, const void *v, const float *d
 
 /*
  * Prefill continuing from a given state per (sequence, head) (chunked prefill; the state
- * S_{-1} above).  initial_state: [S][H][D][D] float32 or NULL (= zeros).  It may not alias
- * final_state.  All other arguments as la_prefill.
+ * S_{-1} above).  Linear attention carries the whole past in the fixed-size state (nabfollower
+ * blog, analogy section), so a sequence prefilled in pieces, each piece starting from the state
+ * the previous one left, gives the same result as one call.  initial_state: [S][H][D][D]
+ * float32 or NULL (= zeros); it is read only and may not overlap final_state or out.  All other
+ * arguments as la_prefill.
  */
 la_status la_prefill_ex(const void *q, const void *k, const void *v, const float *decay,
                         const int32_t *cu_seqlens, const float *initial_state, void *out,
@@ -198,10 +215,14 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
                             size_t workspace_bytes, void *stream);
 
 /*
- * One recurrent decode step for Bt independent sequences (one new token each):
+ * One recurrent decode step for Bt independent sequences (one new token each).  Decoding keeps
+ * only the fixed-size state, so each token costs the same whatever the context length
+ * (nabfollower blog, analogy section), and it runs as its own path beside prefill (digest,
+ * section 3):
  *   S' = lambda S + k^T v ;  o = q S' ;  state <- S'   (in place)
  *   q, k, v in [Bt][H][D] dtype; decay [H] float32; state in/out [Bt][H][D][D] float32;
- *   out [Bt][H][D] dtype.  Bt >= 0 (0 is a no-op).
+ *   out [Bt][H][D] dtype.  Bt >= 0 (0 is a no-op).  state and out must not overlap each other
+ *   or q, k, v, decay.
  */
 la_status la_decode_step(const void *q, const void *k, const void *v, const float *decay,
                          float *state, void *out, int32_t Bt, int32_t H, int32_t D,

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "la_internal.h"
@@ -35,22 +36,62 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 size_t elem_bytes(la_dtype dtype) { return dtype == LA_BF16 ? 2 : 4; }
 
-// out must not overlap q, k or v ([n][H][D] each); state buffers ([S][H][D][D] fp32) must not
-// overlap each other or the activations.
-la_status check_aliasing(const void *q, const void *k, const void *v, const void *out,
-                         int64_t n, const float *st_a, const float *st_b, int64_t nst, int32_t H,
-                         int32_t D, la_dtype dtype) {
-  const size_t act = (size_t)n * H * D * elem_bytes(dtype);
-  const size_t st = (size_t)nst * H * D * D * sizeof(float);
-  const void *in[3] = {q, k, v};
-  for (const void *x : in)
-    if (overlaps(out, act, x, act)) return fail(LA_ERR_INVALID_ARG, "out overlaps q, k or v");
-  const void *acts[4] = {q, k, v, out};
-  for (const float *s : {st_a, st_b})
-    for (const void *x : acts)
-      if (overlaps(s, st, x, act)) return fail(LA_ERR_INVALID_ARG, "a state buffer overlaps an activation");
-  if (overlaps(st_a, st, st_b, st)) return fail(LA_ERR_INVALID_ARG, "state buffers overlap");
+// Callers may pass any int as a dtype; reading a value outside the enumerators through the enum
+// type is undefined in C++, so every entry point checks the argument's bytes first and only
+// then uses it as an la_dtype.
+int dtype_code(const la_dtype &d) {
+  int v;
+  std::memcpy(&v, &d, sizeof v);
+  return v;
+}
+bool valid_dtype(const la_dtype &d) {
+  const int v = dtype_code(d);
+  return v == LA_F32 || v == LA_BF16;
+}
+#define LA_CHECK_DTYPE(d)                                                                  \
+  do {                                                                                     \
+    if (!valid_dtype(d)) return fail(LA_ERR_UNSUPPORTED, "unknown dtype %d", dtype_code(d)); \
+  } while (0)
+
+// A buffer argument of a call: its byte range and its name for the error message.
+struct Buf {
+  const void *p;
+  size_t n;
+  const char *name;
+};
+
+// Every buffer a call writes must be disjoint from every other buffer of the call, read or
+// written (a kernel that writes one while another workgroup still reads or writes it would
+// give wrong results with no error); buffers that are only read may share memory.
+la_status check_disjoint(std::initializer_list<Buf> written, std::initializer_list<Buf> read) {
+  for (const Buf *w = written.begin(); w != written.end(); ++w) {
+    for (const Buf *w2 = w + 1; w2 != written.end(); ++w2)
+      if (overlaps(w->p, w->n, w2->p, w2->n))
+        return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", w->name, w2->name);
+    for (const Buf &r : read)
+      if (overlaps(w->p, w->n, r.p, r.n))
+        return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", w->name, r.name);
+  }
   return LA_OK;
+}
+
+// Byte sizes of the argument kinds.
+size_t act_bytes(int64_t n, int32_t H, int32_t D, la_dtype dtype) {
+  return (size_t)n * H * D * elem_bytes(dtype);
+}
+size_t state_bytes(int64_t n, int32_t H, int32_t D) { return (size_t)n * H * D * D * sizeof(float); }
+size_t cu_bytes(const int32_t *cu, int32_t S) { return cu ? (size_t)(S + 1) * sizeof(int32_t) : 0; }
+
+// The prefill's buffers (plus the split workspace, when given): out and final_state are written.
+la_status check_prefill_buffers(const void *q, const void *k, const void *v, const float *decay,
+                                const int32_t *cu, const float *init, const void *out,
+                                const float *fs, const void *ws, size_t ws_bytes, int64_t T,
+                                int32_t S, int32_t H, int32_t D, la_dtype dtype) {
+  const size_t act = act_bytes(T, H, D, dtype), st = state_bytes(S, H, D);
+  return check_disjoint({{out, act, "out"}, {fs, st, "final_state"}, {ws, ws_bytes, "workspace"}},
+                        {{q, act, "q"}, {k, act, "k"}, {v, act, "v"},
+                         {decay, (size_t)H * sizeof(float), "decay"},
+                         {cu, cu_bytes(cu, S), "cu_seqlens"}, {init, st, "initial_state"}});
 }
 
 constexpr int kMaxDevices = 64;
@@ -81,7 +122,6 @@ la_status check_device(int *cus = nullptr) {
 
 la_status check_common(const void *q, const void *k, const void *v, const float *decay,
                        const void *out, int64_t ntok, int32_t H, int32_t D, la_dtype dtype) {
-  if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (D != 64 && D != 128) return fail(LA_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", D);
   if (H < 1) return fail(LA_ERR_INVALID_ARG, "H = %d < 1", H);
   if (H > 65536) return fail(LA_ERR_INVALID_ARG, "H = %d > 65536", H);
@@ -159,7 +199,11 @@ extern "C" {
 int32_t la_abi_version(void) { return LA_ABI_VERSION; }
 
 const char *la_status_str(la_status s) {
-  switch (s) {
+  // Callers may pass any int; reading a value outside the enumerators through the enum type is
+  // undefined in C++, so the argument's bytes are read as an int.
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case LA_OK: return "LA_OK";
     case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
     case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
@@ -175,15 +219,15 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
                         float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
                         la_dtype dtype, void *stream) {
   g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
   la_status st = check_common(q, k, v, decay, out, T, H, D, dtype);
   if (st != LA_OK) return st;
   if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
   if (cu_seqlens == nullptr && S != 1)
     return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
   if ((long long)S * H * (D / 32) > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "S*H too large");
-  if (initial_state != nullptr && initial_state == final_state)
-    return fail(LA_ERR_INVALID_ARG, "initial_state aliases final_state");
-  st = check_aliasing(q, k, v, out, T, initial_state, final_state, S, H, D, dtype);
+  st = check_prefill_buffers(q, k, v, decay, cu_seqlens, initial_state, out, final_state, nullptr,
+                             0, T, S, H, D, dtype);
   if (st != LA_OK) return st;
   if (final_state == nullptr && (T == 0)) return LA_OK;  // nothing to compute or write
   st = check_device();
@@ -211,6 +255,8 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
 la_status la_prefill(const void *q, const void *k, const void *v, const float *decay,
                      const int32_t *cu_seqlens, void *out, float *final_state, int64_t T,
                      int32_t S, int32_t H, int32_t D, la_dtype dtype, void *stream) {
+  g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
   return la_prefill_ex(q, k, v, decay, cu_seqlens, nullptr, out, final_state, T, S, H, D, dtype,
                        stream);
 }
@@ -223,8 +269,8 @@ size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t 
 
 int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
                                     int32_t compute_units) {
+  if (!valid_dtype(dtype)) return 0;
   if (T <= 0 || S < 1 || H < 1 || (D != 64 && D != 128) || compute_units < 1) return 0;
-  if (dtype != LA_BF16 && dtype != LA_F32) return 0;
   const int64_t slices = D / 32;
   if ((int64_t)S * H * slices >= compute_units) return 0;  // the plain launch fills the device
   const int64_t blocks = (T + 63) / 64;
@@ -252,6 +298,7 @@ int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, 
 }
 
 int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype) {
+  if (!valid_dtype(dtype)) return 0;
   int cus = 0;
   if (check_device(&cus) != LA_OK || cus <= 0) return 0;
   return la_prefill_split_blocks_for(T, S, H, D, dtype, cus);
@@ -263,15 +310,15 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
                            la_dtype dtype, int32_t seg_blocks, void *workspace,
                            size_t workspace_bytes, void *stream) {
   g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
   la_status st = check_common(q, k, v, decay, out, T, H, D, dtype);
   if (st != LA_OK) return st;
   if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
   if (cu_seqlens == nullptr && S != 1)
     return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
-  if (initial_state != nullptr && initial_state == final_state)
-    return fail(LA_ERR_INVALID_ARG, "initial_state aliases final_state");
   if (seg_blocks < 1) return fail(LA_ERR_INVALID_ARG, "seg_blocks = %d < 1", seg_blocks);
-  st = check_aliasing(q, k, v, out, T, initial_state, final_state, S, H, D, dtype);
+  st = check_prefill_buffers(q, k, v, decay, cu_seqlens, initial_state, out, final_state, nullptr,
+                             0, T, S, H, D, dtype);
   if (st != LA_OK) return st;
   if (T > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "split prefill needs T < 2^31");
   if (T == 0)  // no segments: final states are the initial states (or zeros)
@@ -286,17 +333,9 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
   if (workspace_bytes < lay.bytes)
     return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
                 lay.bytes);
-  {
-    const size_t act = (size_t)T * H * D * elem_bytes(dtype);
-    const size_t stb = (size_t)S * H * D * D * sizeof(float);
-    if (overlaps(workspace, lay.bytes, q, act) || overlaps(workspace, lay.bytes, k, act) ||
-        overlaps(workspace, lay.bytes, v, act) || overlaps(workspace, lay.bytes, out, act) ||
-        overlaps(workspace, lay.bytes, initial_state, stb) ||
-        overlaps(workspace, lay.bytes, final_state, stb) ||
-        overlaps(workspace, lay.bytes, decay, (size_t)H * sizeof(float)) ||
-        overlaps(workspace, lay.bytes, cu_seqlens, (size_t)(S + 1) * sizeof(int32_t)))
-      return fail(LA_ERR_INVALID_ARG, "workspace overlaps an argument buffer");
-  }
+  st = check_prefill_buffers(q, k, v, decay, cu_seqlens, initial_state, out, final_state,
+                             workspace, lay.bytes, T, S, H, D, dtype);
+  if (st != LA_OK) return st;
   st = check_device();
   if (st != LA_OK) return st;
 
@@ -347,34 +386,27 @@ la_status check_backward(const void *q, const void *k, const void *v, const floa
                          const int32_t *cu_seqlens, const float *initial_state,
                          const void *d_out, const float *d_final_state, const void *dq,
                          const void *dk, const void *dv, const float *d_initial_state,
-                         int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype) {
+                         const void *ws, size_t ws_bytes, int64_t T, int32_t S, int32_t H,
+                         int32_t D, la_dtype dtype) {
   la_status st = check_common(q, k, v, decay, d_out, T, H, D, dtype);
   if (st != LA_OK) return st;
   if (T > 0) {
     if (!dq || !dk || !dv) return fail(LA_ERR_INVALID_ARG, "dq, dk or dv is NULL");
     if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
       return fail(LA_ERR_INVALID_ARG, "dq, dk and dv must be 16-byte aligned");
-    const size_t act = (size_t)T * H * D * elem_bytes(dtype);
-    const void *in[4] = {q, k, v, d_out};
-    const void *grad[3] = {dq, dk, dv};
-    for (const void *g : grad) {
-      for (const void *x : in)
-        if (overlaps(g, act, x, act)) return fail(LA_ERR_INVALID_ARG, "a gradient output overlaps an input");
-    }
-    if (overlaps(dq, act, dk, act) || overlaps(dq, act, dv, act) || overlaps(dk, act, dv, act))
-      return fail(LA_ERR_INVALID_ARG, "dq, dk and dv must not overlap");
   }
   if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
   if (cu_seqlens == nullptr && S != 1)
     return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
   if ((long long)S * H * (D / 32) > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "S*H too large");
-  {
-    const size_t stb = (size_t)S * H * D * D * sizeof(float);
-    if (overlaps(d_initial_state, stb, initial_state, stb) ||
-        overlaps(d_initial_state, stb, d_final_state, stb))
-      return fail(LA_ERR_INVALID_ARG, "d_initial_state overlaps a state input");
-  }
-  return LA_OK;
+  const size_t act = act_bytes(T, H, D, dtype), stb = state_bytes(S, H, D);
+  return check_disjoint({{dq, act, "dq"}, {dk, act, "dk"}, {dv, act, "dv"},
+                         {d_initial_state, stb, "d_initial_state"}, {ws, ws_bytes, "workspace"}},
+                        {{q, act, "q"}, {k, act, "k"}, {v, act, "v"}, {d_out, act, "d_out"},
+                         {decay, (size_t)H * sizeof(float), "decay"},
+                         {cu_seqlens, cu_bytes(cu_seqlens, S), "cu_seqlens"},
+                         {initial_state, stb, "initial_state"},
+                         {d_final_state, stb, "d_final_state"}});
 }
 }  // namespace
 
@@ -386,8 +418,9 @@ la_status la_backward(const void *q, const void *k, const void *v, const float *
                       float *d_initial_state, int64_t T, int32_t S, int32_t H, int32_t D,
                       la_dtype dtype, void *stream) {
   g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
   la_status st = check_backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state,
-                                dq, dk, dv, d_initial_state, T, S, H, D, dtype);
+                                dq, dk, dv, d_initial_state, nullptr, 0, T, S, H, D, dtype);
   if (st != LA_OK) return st;
   if (T == 0 && d_initial_state == nullptr) return LA_OK;
   st = check_device();
@@ -450,8 +483,9 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
                             int32_t D, la_dtype dtype, int32_t seg_blocks, void *workspace,
                             size_t workspace_bytes, void *stream) {
   g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
   la_status st = check_backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state,
-                                dq, dk, dv, d_initial_state, T, S, H, D, dtype);
+                                dq, dk, dv, d_initial_state, nullptr, 0, T, S, H, D, dtype);
   if (st != LA_OK) return st;
   if (seg_blocks < 1) return fail(LA_ERR_INVALID_ARG, "seg_blocks = %d < 1", seg_blocks);
   if (T > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "split backward needs T < 2^31");
@@ -467,20 +501,9 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
   if (workspace_bytes < lay.bytes)
     return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
                 lay.bytes);
-  {
-    const size_t act = (size_t)T * H * D * elem_bytes(dtype);
-    const size_t stb = (size_t)S * H * D * D * sizeof(float);
-    const void *acts[7] = {q, k, v, d_out, dq, dk, dv};
-    for (const void *x : acts)
-      if (overlaps(workspace, lay.bytes, x, act))
-        return fail(LA_ERR_INVALID_ARG, "workspace overlaps an argument buffer");
-    if (overlaps(workspace, lay.bytes, initial_state, stb) ||
-        overlaps(workspace, lay.bytes, d_final_state, stb) ||
-        overlaps(workspace, lay.bytes, d_initial_state, stb) ||
-        overlaps(workspace, lay.bytes, decay, (size_t)H * sizeof(float)) ||
-        overlaps(workspace, lay.bytes, cu_seqlens, (size_t)(S + 1) * sizeof(int32_t)))
-      return fail(LA_ERR_INVALID_ARG, "workspace overlaps an argument buffer");
-  }
+  st = check_backward(q, k, v, decay, cu_seqlens, initial_state, d_out, d_final_state, dq, dk, dv,
+                      d_initial_state, workspace, lay.bytes, T, S, H, D, dtype);
+  if (st != LA_OK) return st;
   st = check_device();
   if (st != LA_OK) return st;
 
@@ -569,14 +592,20 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const floa
                          float *state, void *out, int32_t Bt, int32_t H, int32_t D,
                          la_dtype dtype, void *stream) {
   g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
   la_status st = check_common(q, k, v, decay, out, Bt, H, D, dtype);
   if (st != LA_OK) return st;
   if (Bt == 0) return LA_OK;
   if (state == nullptr) return fail(LA_ERR_INVALID_ARG, "state is NULL");
   if (!aligned16(state)) return fail(LA_ERR_INVALID_ARG, "state must be 16-byte aligned");
   if ((long long)Bt * H > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "Bt*H too large");
-  st = check_aliasing(q, k, v, out, Bt, state, nullptr, Bt, H, D, dtype);
-  if (st != LA_OK) return st;
+  {
+    const size_t act = act_bytes(Bt, H, D, dtype);
+    st = check_disjoint({{state, state_bytes(Bt, H, D), "state"}, {out, act, "out"}},
+                        {{q, act, "q"}, {k, act, "k"}, {v, act, "v"},
+                         {decay, (size_t)H * sizeof(float), "decay"}});
+    if (st != LA_OK) return st;
+  }
   st = check_device();
   if (st != LA_OK) return st;
   LaDecodeArgs a;
@@ -599,6 +628,7 @@ la_status la_decode_tokens(const void *q, const void *k, const void *v, const fl
                            float *state, void *out, int32_t Bt, int32_t m, int32_t H, int32_t D,
                            la_dtype dtype, void *stream) {
   g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
   if (m < 1) return fail(LA_ERR_INVALID_ARG, "m = %d < 1 tokens per sequence", m);
   if (Bt < 0) return fail(LA_ERR_INVALID_ARG, "negative batch %d", Bt);
   la_status st = check_common(q, k, v, decay, out, (int64_t)Bt * m, H, D, dtype);
@@ -608,13 +638,11 @@ la_status la_decode_tokens(const void *q, const void *k, const void *v, const fl
   if (!aligned16(state)) return fail(LA_ERR_INVALID_ARG, "state must be 16-byte aligned");
   if ((long long)Bt * H > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "Bt*H too large");
   {
-    const size_t act = (size_t)Bt * m * H * D * elem_bytes(dtype);
-    const size_t stb = (size_t)Bt * H * D * D * sizeof(float);
-    const void *acts[4] = {q, k, v, out};
-    for (int i = 0; i < 3; ++i)
-      if (overlaps(out, act, acts[i], act)) return fail(LA_ERR_INVALID_ARG, "out overlaps q, k or v");
-    for (const void *x : acts)
-      if (overlaps(state, stb, x, act)) return fail(LA_ERR_INVALID_ARG, "state overlaps an activation");
+    const size_t act = act_bytes((int64_t)Bt * m, H, D, dtype);
+    st = check_disjoint({{state, state_bytes(Bt, H, D), "state"}, {out, act, "out"}},
+                        {{q, act, "q"}, {k, act, "k"}, {v, act, "v"},
+                         {decay, (size_t)H * sizeof(float), "decay"}});
+    if (st != LA_OK) return st;
   }
   st = check_device();
   if (st != LA_OK) return st;

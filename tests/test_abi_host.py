@@ -68,12 +68,26 @@ def _prefill(lib, q=P, k=P, v=P, decay=P, cu=None, out=P2, fs=None, T=64, S=1, H
     (dict(q=MISALIGNED), 1), (dict(init=P2, fs=P2), 1),
     # byte-range overlaps: q, k, v are 64 x 2 x 128 bf16 = 32 KiB, states 2 x 64 KiB
     (dict(out=ctypes.c_void_p(0x100000 + 0x7ff0)), 1), (dict(v=ctypes.c_void_p(0x200000 - 0x10)), 1),
-    (dict(fs=ctypes.c_void_p(0x204000)), 1), (dict(init=ctypes.c_void_p(0x100010)), 1),
+    (dict(fs=ctypes.c_void_p(0x204000)), 1), (dict(init=ctypes.c_void_p(0x200010)), 1),
     (dict(init=ctypes.c_void_p(0x300000), fs=ctypes.c_void_p(0x310000)), 1),
+    # decay ([H] fp32) or cu_seqlens ([S+1] int32) inside a written buffer
+    (dict(decay=ctypes.c_void_p(0x200000 + 0x100)), 1),
+    (dict(cu=ctypes.c_void_p(0x700000 + 0x40), fs=ctypes.c_void_p(0x700000)), 1),
+    (dict(decay=ctypes.c_void_p(0x700000 + 0x8), fs=ctypes.c_void_p(0x700000)), 1),
 ])
 def test_prefill_validation(lib, kwargs, status):
     assert _prefill(lib, **kwargs) == status
     assert lib.la_last_error() != b""
+
+
+def test_read_only_buffers_may_share_memory(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    # q, k, v, decay and the initial state all read: overlapping them is no hazard, so
+    # validation passes and the device check (no GPU here) reports the HIP error.
+    assert _prefill(lib, init=ctypes.c_void_p(0x100010), decay=ctypes.c_void_p(0x100020)) == 3
 
 
 def test_prefill_empty_is_noop(lib):
@@ -159,9 +173,9 @@ G1, G2, G3 = ctypes.c_void_p(0x400000), ctypes.c_void_p(0x500000), ctypes.c_void
 
 
 def _backward(lib, dq=G1, dk=G2, dv=G3, d_out=P2, dinit=None, init=None, dfs=None, T=64, S=1,
-              D=128, q=P):
-    return lib.la_backward(q, P, P, P, None, init, d_out, dfs, dq, dk, dv, dinit, T, S, 2, D, 1,
-                           None)
+              D=128, q=P, decay=P):
+    return lib.la_backward(q, P, P, decay, None, init, d_out, dfs, dq, dk, dv, dinit, T, S, 2, D,
+                           1, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -217,20 +231,35 @@ def test_adjacent_buffers_are_not_overlaps(lib):
 @pytest.mark.parametrize("kwargs", [
     dict(out=ctypes.c_void_p(0x100100)), dict(state=ctypes.c_void_p(0x700000)),
     dict(state=ctypes.c_void_p(0x100000 - 0x10)),
+    # decay inside the state (read while other workgroups update it) or inside out
+    dict(decay=ctypes.c_void_p(0x200000 + 0x1000)), dict(decay=ctypes.c_void_p(0x700000 + 0x10)),
 ])
 def test_decode_overlap_rejected(lib, kwargs):
-    a = dict(q=P, k=P, v=P, state=P2, out=OUT)
+    a = dict(q=P, k=P, v=P, decay=P, state=P2, out=OUT)
     a.update(kwargs)
-    assert lib.la_decode_step(a["q"], a["k"], a["v"], P, a["state"], a["out"], 4, 2, 128, 1,
-                              None) == 1
+    assert lib.la_decode_step(a["q"], a["k"], a["v"], a["decay"], a["state"], a["out"], 4, 2, 128,
+                              1, None) == 1
     assert b"overlap" in lib.la_last_error()
-    assert lib.la_decode_tokens(a["q"], a["k"], a["v"], P, a["state"], a["out"], 4, 3, 2, 128, 1,
-                                None) == 1
+    assert lib.la_decode_tokens(a["q"], a["k"], a["v"], a["decay"], a["state"], a["out"], 4, 3, 2,
+                                128, 1, None) == 1
+
+
+S1, S2 = ctypes.c_void_p(0x900000), ctypes.c_void_p(0xa00000)  # state-sized (2 x 64 KiB)
 
 
 @pytest.mark.parametrize("kwargs", [
     dict(dq=ctypes.c_void_p(0x200000 + 0x4000)), dict(dv=ctypes.c_void_p(0x500000 + 0x7f00)),
     dict(dk=ctypes.c_void_p(0x100000 + 0x10)),
+    # d_initial_state against every activation and gradient buffer
+    dict(dinit=ctypes.c_void_p(0x400000 + 0x100)), dict(dinit=ctypes.c_void_p(0x500000)),
+    dict(dinit=ctypes.c_void_p(0x600000 + 0x10)), dict(dinit=ctypes.c_void_p(0x100000)),
+    dict(dinit=ctypes.c_void_p(0x200000 + 0x40)),
+    # the state inputs inside a gradient buffer
+    dict(init=ctypes.c_void_p(0x400000), dinit=S1), dict(dfs=ctypes.c_void_p(0x600000), dinit=S1),
+    dict(init=ctypes.c_void_p(0x500000 + 0x100)), dict(dfs=ctypes.c_void_p(0x400000 + 0x7000)),
+    # decay inside a written buffer
+    dict(decay=ctypes.c_void_p(0x400000 + 0x20)), dict(decay=ctypes.c_void_p(0x900000 + 0x20),
+                                                       dinit=S1),
 ])
 def test_backward_overlap_rejected(lib, kwargs):
     assert _backward(lib, **kwargs) == 1
