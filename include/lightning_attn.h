@@ -138,6 +138,27 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
                            la_dtype dtype, int32_t seg_blocks, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * la_prefill_split without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * segment states and segment table live in a static device array of
+ * LA_SPLIT_STATIC_SCRATCH_BYTES that every device the library runs on holds from the library's
+ * load until the process ends.  The call allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine); the caller still owns every other buffer.  Same arguments,
+ * result and errors as la_prefill_split otherwise, plus LA_ERR_INVALID_ARG when these sizes
+ * need more than LA_SPLIT_STATIC_SCRATCH_BYTES of workspace
+ * (la_prefill_split_workspace_size(T, S, H, D, seg_blocks) > LA_SPLIT_STATIC_SCRATCH_BYTES).
+ * All calls on one device share its scratch: calls that overlap in time on one device (two
+ * streams, two host threads) race and give wrong results; order them on one stream.  The
+ * scratch needs no initial contents.
+ */
+#define LA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+la_status la_prefill_split_static(const void *q, const void *k, const void *v,
+                                  const float *decay, const int32_t *cu_seqlens,
+                                  const float *initial_state, void *out, float *final_state,
+                                  int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
+                                  int32_t seg_blocks, void *stream);
+
 /* Workspace bytes la_prefill_split and la_backward_split need for these sizes (0 for invalid
  * sizes).  The bound holds for any valid cu_seqlens: (ceil(T / (64 seg_blocks)) + S - 1) states
  * of H*D*D floats plus the segment table. */

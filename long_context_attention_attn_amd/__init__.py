@@ -51,7 +51,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
             out: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None,
             return_final_state: bool = True,
-            split: Union[None, str, int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            split: Union[None, str, int] = None,
+            static_scratch: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Lightning-attention prefill over packed sequences.
 
     q, k, v: [T, H, D] bf16 or fp32 (same dtype), contiguous, on a gfx950 device.
@@ -63,6 +64,10 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
     with segments of n 64-token blocks (a workspace is allocated with torch); "auto" = the
     sequence split with the segment length the library suggests for this device, or the plain
     scan when it suggests none.  All give the same result up to rounding order.
+    static_scratch: with a sequence split, keep its segment states in the library's static
+    device scratch (la_prefill_split_static) instead of a torch-allocated workspace, so the
+    library call allocates nothing; needs la_prefill_split_workspace_size <= 32 MiB.  Calls
+    that overlap in time on one device share that scratch and must be ordered on one stream.
     """
     device = q.device
     if q.dim() != 3:
@@ -107,7 +112,10 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
             0 if cu_seqlens is None else cu_seqlens.data_ptr(),
             0 if initial_state is None else initial_state.data_ptr(),
             out.data_ptr(), 0 if final_state is None else final_state.data_ptr())
-    if seg_blocks > 0:
+    if seg_blocks > 0 and static_scratch:
+        _lib.prefill_split_static(*ptrs, T, S, H, D, _DTYPES[dtype], seg_blocks,
+                                  _stream_ptr(device))
+    elif seg_blocks > 0:
         nbytes = _lib.prefill_split_workspace_size(T, S, H, D, seg_blocks)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         # ws is allocated on the current stream, so torch's caching allocator reuses its memory

@@ -22,6 +22,7 @@ ABI_VERSION = 2  # LA_ABI_VERSION of include/lightning_attn.h
 
 # Every symbol declared in include/lightning_attn.h.
 EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_split",
+           "la_prefill_split_static",
            "la_prefill_split_workspace_size", "la_prefill_split_blocks",
            "la_prefill_split_blocks_for", "la_backward",
            "la_backward_split",
@@ -76,6 +77,9 @@ def load():
         lib.la_prefill_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
                                          ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
         lib.la_prefill_split.restype = ctypes.c_int
+        lib.la_prefill_split_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
+                                                ctypes.c_int, i32, vp]
+        lib.la_prefill_split_static.restype = ctypes.c_int
         lib.la_prefill_split_workspace_size.argtypes = [i64, i32, i32, i32, i32]
         lib.la_prefill_split_workspace_size.restype = ctypes.c_size_t
         lib.la_prefill_split_blocks.argtypes = [i64, i32, i32, i32, ctypes.c_int]
@@ -128,6 +132,18 @@ def prefill_split(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T
     _raise(load().la_prefill_split(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens),
                                    _p(initial_state), _p(out), _p(final_state), T, S, H, D, dtype,
                                    seg_blocks, _p(workspace), workspace_bytes, _p(stream)))
+
+
+def prefill_split_static(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H, D,
+                         dtype, seg_blocks, stream):
+    _raise(load().la_prefill_split_static(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens),
+                                          _p(initial_state), _p(out), _p(final_state), T, S, H,
+                                          D, dtype, seg_blocks, _p(stream)))
+
+
+# LA_SPLIT_STATIC_SCRATCH_BYTES of include/lightning_attn.h (the static scratch of
+# la_prefill_split_static, per device)
+SPLIT_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 def prefill_split_workspace_size(T, S, H, D, seg_blocks) -> int:

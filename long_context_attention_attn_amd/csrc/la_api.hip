@@ -95,6 +95,8 @@ la_status check_prefill_buffers(const void *q, const void *k, const void *v, con
 }
 
 constexpr int kMaxDevices = 64;
+// Size of the static scratch of la_prefill_split_static (per device).
+constexpr size_t kScratchBytes = LA_SPLIT_STATIC_SCRATCH_BYTES;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];   // 1 = gfx950, 0 = other arch
 int g_dev_cus[kMaxDevices];  // compute units
@@ -192,6 +194,124 @@ double block_cost(la_dtype dtype, int32_t D, double w, double bytes) {
   const double h = D == 64 ? LA_COST_AT(kBf16D64Hbm, w) : LA_COST_AT(kBf16D128Hbm, w);
   return (1 - f) * c + f * h;
 }
+}  // namespace
+
+// Scratch of the allocation-free split prefill (la_prefill_split_static): the segment states and
+// segment table that la_prefill_split keeps in the caller's workspace.  Every device the library
+// runs on holds its own copy from module load until the process ends.  In host code the name is
+// only a host-side stand-in; kernels get the device address from scratch_address().
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch, looked up once per device with that device
+// current.
+la_status scratch_address(void **p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LA_ERR_HIP, "device index %d out of range", dev);
+  std::call_once(g_scratch_once[dev], [&]() {
+    g_scratch_ptr[dev] = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr)
+    return fail(LA_ERR_HIP, "hipGetSymbolAddress(scratch): %s",
+                hipGetErrorString(g_scratch_err[dev]));
+  *p = g_scratch_ptr[dev];
+  return LA_OK;
+}
+
+// The split prefill behind la_prefill_split (the caller's workspace) and
+// la_prefill_split_static (the library's static scratch, static_scratch = true: workspace and
+// workspace_bytes are ignored).  The dtype has been checked.
+la_status prefill_split_impl(const void *q, const void *k, const void *v, const float *decay,
+                             const int32_t *cu_seqlens, const float *initial_state, void *out,
+                             float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                             la_dtype dtype, int32_t seg_blocks, void *workspace,
+                             size_t workspace_bytes, bool static_scratch, void *stream) {
+  la_status st = check_common(q, k, v, decay, out, T, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
+  if (cu_seqlens == nullptr && S != 1)
+    return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
+  if (seg_blocks < 1) return fail(LA_ERR_INVALID_ARG, "seg_blocks = %d < 1", seg_blocks);
+  st = check_prefill_buffers(q, k, v, decay, cu_seqlens, initial_state, out, final_state, nullptr,
+                             0, T, S, H, D, dtype);
+  if (st != LA_OK) return st;
+  if (T > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "split prefill needs T < 2^31");
+  if (T == 0)  // no segments: final states are the initial states (or zeros)
+    return la_prefill_ex(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H,
+                         D, dtype, stream);
+  const SplitLayout lay = split_layout(T, S, H, D, seg_blocks);
+  if (lay.cap * H * (D / 32) > 0x7fffffffLL || (long long)S * H * (D * D / 256) > 0x7fffffffLL)
+    return fail(LA_ERR_INVALID_ARG, "too many segments");
+  if (static_scratch) {
+    if (lay.bytes > kScratchBytes)
+      return fail(LA_ERR_INVALID_ARG,
+                  "these sizes need %zu bytes of split workspace; the static scratch holds %zu "
+                  "(use la_prefill_split with a caller workspace, or longer segments)",
+                  lay.bytes, kScratchBytes);
+    st = check_device();
+    if (st != LA_OK) return st;
+    st = scratch_address(&workspace);
+    if (st != LA_OK) return st;
+  } else {
+    if (workspace == nullptr) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(LA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (workspace_bytes < lay.bytes)
+      return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                  lay.bytes);
+    st = check_prefill_buffers(q, k, v, decay, cu_seqlens, initial_state, out, final_state,
+                               workspace, lay.bytes, T, S, H, D, dtype);
+    if (st != LA_OK) return st;
+    st = check_device();
+    if (st != LA_OK) return st;
+  }
+
+  char *ws = static_cast<char *>(workspace);
+  float *states = reinterpret_cast<float *>(ws + lay.states);
+  int32_t *seg_cu = reinterpret_cast<int32_t *>(ws + lay.seg_cu);
+  int32_t *seq_seg0 = reinterpret_cast<int32_t *>(ws + lay.seq_seg0);
+  const int32_t cap = (int32_t)lay.cap;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto prefill = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
+
+  hipError_t e = la_launch_seg_table(cu_seqlens, T, S, (int64_t)seg_blocks * 64, cap, seg_cu,
+                                     seq_seg0, nullptr, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment table launch: %s", hipGetErrorString(e));
+  // Segment states from zero: only k and v are read.
+  LaPrefillArgs a{};
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.cu_seqlens = seg_cu;
+  a.final_state = states;
+  a.T = T;
+  a.S = cap;
+  a.H = H;
+  a.D = D;
+  a.state_only = true;
+  e = dtype == LA_BF16 ? la_launch_segment_states_bf16(a, (int64_t)seg_blocks * 64, s) : prefill(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment state launch: %s", hipGetErrorString(e));
+  e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, final_state,
+                        false, false, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  // Every segment from its incoming state.
+  a.q = q;
+  a.out = out;
+  a.initial_state = states;
+  a.final_state = nullptr;
+  a.state_only = false;
+  e = prefill(a, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment prefill launch: %s", hipGetErrorString(e));
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,71 +431,19 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
                            size_t workspace_bytes, void *stream) {
   g_err[0] = '\0';
   LA_CHECK_DTYPE(dtype);
-  la_status st = check_common(q, k, v, decay, out, T, H, D, dtype);
-  if (st != LA_OK) return st;
-  if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
-  if (cu_seqlens == nullptr && S != 1)
-    return fail(LA_ERR_INVALID_ARG, "cu_seqlens is NULL but S = %d (must be 1)", S);
-  if (seg_blocks < 1) return fail(LA_ERR_INVALID_ARG, "seg_blocks = %d < 1", seg_blocks);
-  st = check_prefill_buffers(q, k, v, decay, cu_seqlens, initial_state, out, final_state, nullptr,
-                             0, T, S, H, D, dtype);
-  if (st != LA_OK) return st;
-  if (T > 0x7fffffffLL) return fail(LA_ERR_INVALID_ARG, "split prefill needs T < 2^31");
-  if (T == 0)  // no segments: final states are the initial states (or zeros)
-    return la_prefill_ex(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H,
-                         D, dtype, stream);
-  const SplitLayout lay = split_layout(T, S, H, D, seg_blocks);
-  if (lay.cap * H * (D / 32) > 0x7fffffffLL || (long long)S * H * (D * D / 256) > 0x7fffffffLL)
-    return fail(LA_ERR_INVALID_ARG, "too many segments");
-  if (workspace == nullptr) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(LA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < lay.bytes)
-    return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
-                lay.bytes);
-  st = check_prefill_buffers(q, k, v, decay, cu_seqlens, initial_state, out, final_state,
-                             workspace, lay.bytes, T, S, H, D, dtype);
-  if (st != LA_OK) return st;
-  st = check_device();
-  if (st != LA_OK) return st;
+  return prefill_split_impl(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H,
+                            D, dtype, seg_blocks, workspace, workspace_bytes, false, stream);
+}
 
-  char *ws = static_cast<char *>(workspace);
-  float *states = reinterpret_cast<float *>(ws + lay.states);
-  int32_t *seg_cu = reinterpret_cast<int32_t *>(ws + lay.seg_cu);
-  int32_t *seq_seg0 = reinterpret_cast<int32_t *>(ws + lay.seq_seg0);
-  const int32_t cap = (int32_t)lay.cap;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto prefill = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
-
-  hipError_t e = la_launch_seg_table(cu_seqlens, T, S, (int64_t)seg_blocks * 64, cap, seg_cu,
-                                     seq_seg0, nullptr, s);
-  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment table launch: %s", hipGetErrorString(e));
-  // Segment states from zero: only k and v are read.
-  LaPrefillArgs a{};
-  a.k = k;
-  a.v = v;
-  a.decay = decay;
-  a.cu_seqlens = seg_cu;
-  a.final_state = states;
-  a.T = T;
-  a.S = cap;
-  a.H = H;
-  a.D = D;
-  a.state_only = true;
-  e = dtype == LA_BF16 ? la_launch_segment_states_bf16(a, (int64_t)seg_blocks * 64, s) : prefill(a, s);
-  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment state launch: %s", hipGetErrorString(e));
-  e = la_launch_combine(decay, seg_cu, seq_seg0, S, H, D, initial_state, states, final_state,
-                        false, false, s);
-  if (e != hipSuccess) return fail(LA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
-  // Every segment from its incoming state.
-  a.q = q;
-  a.out = out;
-  a.initial_state = states;
-  a.final_state = nullptr;
-  a.state_only = false;
-  e = prefill(a, s);
-  if (e != hipSuccess) return fail(LA_ERR_HIP, "segment prefill launch: %s", hipGetErrorString(e));
-  return LA_OK;
+la_status la_prefill_split_static(const void *q, const void *k, const void *v,
+                                  const float *decay, const int32_t *cu_seqlens,
+                                  const float *initial_state, void *out, float *final_state,
+                                  int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
+                                  int32_t seg_blocks, void *stream) {
+  g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
+  return prefill_split_impl(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H,
+                            D, dtype, seg_blocks, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

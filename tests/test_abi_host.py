@@ -370,3 +370,47 @@ def test_split_suggestion_rules(lib):
     for args in ((0, 1, 8, 128, 1, 256), (4096, 0, 8, 128, 1, 256), (4096, 1, 0, 128, 1, 256),
                  (4096, 1, 8, 96, 1, 256), (4096, 1, 8, 128, 7, 256), (4096, 1, 8, 128, 1, 0)):
         assert f(*args) == 0, args
+
+
+FAR_IN, FAR_OUT = ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x40000000)  # 768 MiB apart
+
+
+def _split_static(lib, T=1000, seg_blocks=4, H=2, D=128, S=1, cu=None, q=FAR_IN, dt=1):
+    return lib.la_prefill_split_static(q, FAR_IN, FAR_IN, P, cu, None, FAR_OUT, None, T, S, H, D,
+                                       dt, seg_blocks, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(seg_blocks=0), 1), (dict(T=1 << 31), 1), (dict(q=None), 1), (dict(D=80), 2),
+    (dict(dt=9), 2), (dict(S=2), 1),
+    # 65,536 tokens x 8 heads in 1-block segments: 1,024 x 8 x 64 KiB of segment states, far
+    # beyond the 32 MiB static scratch
+    (dict(T=65536, H=8, seg_blocks=1), 1),
+])
+def test_split_static_validation(lib, kwargs, status):
+    assert _split_static(lib, **kwargs) == status
+    assert lib.la_last_error() != b""
+    if kwargs.get("T") == 65536:
+        assert b"static scratch" in lib.la_last_error()
+
+
+def test_split_static_limit(lib):
+    from long_context_attention_attn_amd import _lib
+
+    # the largest single-sequence 8-head D=128 split that fits: its workspace is at most the
+    # scratch; one more segment does not fit and is rejected before any HIP call
+    cap = _lib.SPLIT_STATIC_SCRATCH_BYTES
+    assert cap == 32 << 20
+    fits = lib.la_prefill_split_workspace_size(64 * 60, 1, 8, 128, 1)
+    over = lib.la_prefill_split_workspace_size(64 * 70, 1, 8, 128, 1)
+    assert fits <= cap < over
+    assert _split_static(lib, T=64 * 70, H=8, seg_blocks=1) == 1
+    assert b"static scratch" in lib.la_last_error()
+
+
+def test_split_static_without_device(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _split_static(lib) == 3
