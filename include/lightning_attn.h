@@ -107,6 +107,25 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
                         la_dtype dtype, void *stream);
 
 /*
+ * Prefill with a chosen block size B (la_prefill_ex with its initial state, plus block_size).
+ * The split into blocks (digest, section 1: left product inside a block, right product across
+ * blocks) is exact algebra for any B, so every B gives the same result up to rounding; B only
+ * trades the number of serial block steps of a scan against the size of each block's intra
+ * product (4 B d + 4 d^2 FLOP per token-head).
+ *   block_size  0 = the default: 64, or for bf16 storage the value of the environment variable
+ *               LA_BLOCK (64 or 128; read once per process; any other value makes bf16 calls
+ *               fail with LA_ERR_INVALID_ARG); la_prefill and la_prefill_ex use this default
+ *               64 or 128 (128: bf16 storage only, else LA_ERR_UNSUPPORTED)
+ * Other arguments, result and errors as la_prefill_ex, plus LA_ERR_INVALID_ARG for any other
+ * block_size.  The sequence-split prefill, the backward and the fp32 path always use B = 64.
+ */
+la_status la_prefill_with_block_size(const void *q, const void *k, const void *v,
+                                     const float *decay, const int32_t *cu_seqlens,
+                                     const float *initial_state, void *out, float *final_state,
+                                     int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
+                                     int32_t block_size, void *stream);
+
+/*
  * Sequence-split prefill: the same result as la_prefill_ex, computed with every sequence cut
  * into segments of seg_blocks * 64 tokens that are scanned in parallel.  Meant for batches with
  * few (sequence, head) pairs, where the plain prefill runs one workgroup per (sequence, head,

@@ -52,7 +52,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
             final_state: Optional[torch.Tensor] = None,
             return_final_state: bool = True,
             split: Union[None, str, int] = None,
-            static_scratch: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            static_scratch: bool = False,
+            block_size: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Lightning-attention prefill over packed sequences.
 
     q, k, v: [T, H, D] bf16 or fp32 (same dtype), contiguous, on a gfx950 device.
@@ -64,6 +65,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
     with segments of n 64-token blocks (a workspace is allocated with torch); "auto" = the
     sequence split with the segment length the library suggests for this device, or the plain
     scan when it suggests none.  All give the same result up to rounding order.
+    block_size: 0 = the library's default, or 64 / 128 tokens per block (128: bf16 only; the
+    sequence split always uses 64).  Every block size gives the same result up to rounding.
     static_scratch: with a sequence split, keep its segment states in the library's static
     device scratch (la_prefill_split_static) instead of a torch-allocated workspace, so the
     library call allocates nothing; needs la_prefill_split_workspace_size <= 32 MiB.  Calls
@@ -123,7 +126,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
         _lib.prefill_split(*ptrs, T, S, H, D, _DTYPES[dtype], seg_blocks, ws.data_ptr(), nbytes,
                            _stream_ptr(device))
     else:
-        _lib.prefill_ex(*ptrs, T, S, H, D, _DTYPES[dtype], _stream_ptr(device))
+        _lib.prefill_with_block_size(*ptrs, T, S, H, D, _DTYPES[dtype], block_size,
+                                     _stream_ptr(device))
     return out, final_state
 
 

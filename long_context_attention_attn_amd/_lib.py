@@ -21,7 +21,8 @@ LA_F32, LA_BF16 = 0, 1
 ABI_VERSION = 2  # LA_ABI_VERSION of include/lightning_attn.h
 
 # Every symbol declared in include/lightning_attn.h.
-EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_split",
+EXPORTS = ("la_abi_version", "la_prefill", "la_prefill_ex", "la_prefill_with_block_size",
+           "la_prefill_split",
            "la_prefill_split_static",
            "la_prefill_split_workspace_size", "la_prefill_split_blocks",
            "la_prefill_split_blocks_for", "la_backward",
@@ -74,6 +75,9 @@ def load():
         lib.la_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
                                       ctypes.c_int, vp]
         lib.la_prefill_ex.restype = ctypes.c_int
+        lib.la_prefill_with_block_size.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32,
+                                                   i32, ctypes.c_int, i32, vp]
+        lib.la_prefill_with_block_size.restype = ctypes.c_int
         lib.la_prefill_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32,
                                          ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
         lib.la_prefill_split.restype = ctypes.c_int
@@ -125,6 +129,13 @@ def prefill_ex(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S
                stream):
     _raise(load().la_prefill_ex(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens), _p(initial_state),
                                 _p(out), _p(final_state), T, S, H, D, dtype, _p(stream)))
+
+
+def prefill_with_block_size(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S,
+                            H, D, dtype, block_size, stream):
+    _raise(load().la_prefill_with_block_size(_p(q), _p(k), _p(v), _p(decay), _p(cu_seqlens),
+                                             _p(initial_state), _p(out), _p(final_state), T, S,
+                                             H, D, dtype, block_size, _p(stream)))
 
 
 def prefill_split(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H, D, dtype,

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
@@ -92,6 +93,22 @@ la_status check_prefill_buffers(const void *q, const void *k, const void *v, con
                         {{q, act, "q"}, {k, act, "k"}, {v, act, "v"},
                          {decay, (size_t)H * sizeof(float), "decay"},
                          {cu, cu_bytes(cu, S), "cu_seqlens"}, {init, st, "initial_state"}});
+}
+
+// Default block size of the bf16 prefill from the environment variable LA_BLOCK (read once):
+// 0 when unset, 64 or 128, -1 for any other value.  Meant for running a test suite at either
+// block size without changing its calls.
+int env_block() {
+  static std::once_flag once;
+  static int value = 0;
+  std::call_once(once, [] {
+    const char *e = std::getenv("LA_BLOCK");
+    if (e == nullptr || *e == '\0') value = 0;
+    else if (std::strcmp(e, "64") == 0) value = 64;
+    else if (std::strcmp(e, "128") == 0) value = 128;
+    else value = -1;
+  });
+  return value;
 }
 
 constexpr int kMaxDevices = 64;
@@ -334,12 +351,22 @@ const char *la_status_str(la_status s) {
 
 const char *la_last_error(void) { return g_err; }
 
-la_status la_prefill_ex(const void *q, const void *k, const void *v, const float *decay,
-                        const int32_t *cu_seqlens, const float *initial_state, void *out,
-                        float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
-                        la_dtype dtype, void *stream) {
+la_status la_prefill_with_block_size(const void *q, const void *k, const void *v,
+                                     const float *decay, const int32_t *cu_seqlens,
+                                     const float *initial_state, void *out, float *final_state,
+                                     int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
+                                     int32_t block_size, void *stream) {
   g_err[0] = '\0';
   LA_CHECK_DTYPE(dtype);
+  if (block_size == 0 && dtype == LA_BF16) {
+    block_size = env_block();
+    if (block_size < 0) return fail(LA_ERR_INVALID_ARG, "LA_BLOCK must be 64 or 128");
+  }
+  if (block_size == 0) block_size = 64;
+  if (block_size != 64 && block_size != 128)
+    return fail(LA_ERR_INVALID_ARG, "block_size = %d not in {0, 64, 128}", block_size);
+  if (block_size == 128 && dtype != LA_BF16)
+    return fail(LA_ERR_UNSUPPORTED, "128-token blocks are built for bf16 storage only");
   la_status st = check_common(q, k, v, decay, out, T, H, D, dtype);
   if (st != LA_OK) return st;
   if (S < 1) return fail(LA_ERR_INVALID_ARG, "S = %d < 1", S);
@@ -367,9 +394,21 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
   a.H = H;
   a.D = D;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = dtype == LA_BF16 ? la_launch_prefill_bf16(a, s) : la_launch_prefill_f32(a, s);
+  hipError_t e = dtype == LA_F32        ? la_launch_prefill_f32(a, s)
+                 : block_size == 128 ? la_launch_prefill_bf16_b128(a, s)
+                                     : la_launch_prefill_bf16(a, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return LA_OK;
+}
+
+la_status la_prefill_ex(const void *q, const void *k, const void *v, const float *decay,
+                        const int32_t *cu_seqlens, const float *initial_state, void *out,
+                        float *final_state, int64_t T, int32_t S, int32_t H, int32_t D,
+                        la_dtype dtype, void *stream) {
+  g_err[0] = '\0';
+  LA_CHECK_DTYPE(dtype);
+  return la_prefill_with_block_size(q, k, v, decay, cu_seqlens, initial_state, out, final_state,
+                                    T, S, H, D, dtype, 0, stream);
 }
 
 la_status la_prefill(const void *q, const void *k, const void *v, const float *decay,

@@ -414,3 +414,52 @@ def test_split_static_without_device(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert _split_static(lib) == 3
+
+
+def _prefill_bs(lib, block_size, dt=1):
+    return lib.la_prefill_with_block_size(P, P, P, P, None, None, P2, None, 64, 1, 2, 128, dt,
+                                          block_size, None)
+
+
+@pytest.mark.parametrize("block_size,dt,status", [
+    (32, 1, 1), (256, 1, 1), (-1, 1, 1), (96, 1, 1),  # only 0, 64 and 128
+    (128, 0, 2),                                        # 128-token blocks: bf16 only
+])
+def test_block_size_validation(lib, block_size, dt, status):
+    assert _prefill_bs(lib, block_size, dt) == status
+    assert lib.la_last_error() != b""
+
+
+def test_block_size_without_device(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    for bs, dt in ((0, 1), (64, 1), (128, 1), (0, 0), (64, 0)):
+        assert _prefill_bs(lib, bs, dt) == 3, (bs, dt)
+
+
+@pytest.mark.parametrize("env,dt,status", [
+    ("96", 1, 1), ("abc", 1, 1),  # an invalid LA_BLOCK fails bf16 calls that use the default
+    ("96", 0, 3),                 # fp32 has one block size and ignores LA_BLOCK
+    ("128", 1, 3), ("64", 1, 3), ("", 1, 3),
+])
+def test_la_block_environment(env, dt, status):
+    """LA_BLOCK sets the default block size of bf16 prefills (read once per process, so each
+    case runs in a child process; no GPU here, so valid calls end at the device check)."""
+    import subprocess
+    import sys
+
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    script = ("import sys, ctypes; sys.path.insert(0, %r)\n"
+              "from long_context_attention_attn_amd import _lib\n"
+              "lib = _lib.load(); P = ctypes.c_void_p(0x100000); O = ctypes.c_void_p(0x200000)\n"
+              "print(lib.la_prefill(P, P, P, P, None, O, None, 64, 1, 2, 128, %d, None))\n"
+              % (ROOT, dt))
+    r = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True,
+                       env=dict(os.environ, LA_BLOCK=env), timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert int(r.stdout.strip().splitlines()[-1]) == status
