@@ -36,7 +36,12 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
 T_PREFILL, H, D = 65536, 64, 128
 BT_DECODE = 256
-BLOCK_FLOP_B = 64              # FLOP accounting at block size 64 (the kernel's block size)
+BLOCK_FLOP_B = 64              # FLOP accounting at block size 64, whatever the kernel's B
+KERNEL_BLOCK = 128             # the bf16 prefill's block size (the library default)
+PREFILL_KERNEL = "prefill_bf16_b128_kernel<128>"
+# sources the committed profiles of that kernel were taken with
+PREFILL_SOURCES = ("long_context_attention_attn_amd/csrc/prefill_bf16_b128.hip",
+                   "long_context_attention_attn_amd/csrc/bf16_tiles.h")
 
 
 def prefill_flop(T, H, D, B=BLOCK_FLOP_B):
@@ -152,13 +157,17 @@ def main():
             "workload": "lightning prefill 1 x 65536 tokens x 64 heads x d128 bf16 "
                         "(lambda 0.9->0.9999, final fp32 states) + decode step 256 seqs x 64 "
                         "heads fp32 128x128 states",
-            "prefill_tokens": T_PREFILL, "heads": H, "head_dim": D, "block": 64,
+            "prefill_tokens": T_PREFILL, "heads": H, "head_dim": D, "block": KERNEL_BLOCK,
             "decode_batch": BT_DECODE,
         },
         "prefill": {
             "ms": pre_avg, "ms_min": min(pre_ms),
             "tokens_per_s": T_PREFILL / (pre_avg / 1e3),
             "tflops": pre_tflops, "pct_bf16_mfma_peak": 100.0 * pre_tflops / BF16_PEAK_TFLOPS,
+            # the FLOP the kernel itself issues at its own block size (intra 4 B d grows with B)
+            "kernel_block": KERNEL_BLOCK,
+            "kernel_flop_per_launch": prefill_flop(T_PREFILL, H, D, KERNEL_BLOCK),
+            "kernel_block_tflops": prefill_flop(T_PREFILL, H, D, KERNEL_BLOCK) / (pre_avg / 1e3) / 1e12,
             "algorithmic_GBps": pre_gbps,
             "flop_per_launch": pf, "bytes_per_launch": pb,
         },
@@ -167,7 +176,7 @@ def main():
             "pct_hbm_peak": 100.0 * dec_gbps / HBM_PEAK_GBPS, "bytes_per_launch": db,
         },
         "roofline": {
-            "bound": "hbm", "kernel": "prefill_bf16_kernel<128, false, false>",
+            "bound": "hbm", "kernel": PREFILL_KERNEL,
             "achieved": pre_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": pre_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
             "achieved_source": "HIP events around the prefill launches of this run",
@@ -339,19 +348,27 @@ def long_prefill_leg(name, dev, iters=5, warmup=2):
             "hbm_frac": gbps / HBM_PEAK_GBPS}
 
 
+def sources_sha256(paths):
+    """sha256 over the concatenated bytes of the given repository files."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
 def committed_trace(nbytes):
     """The prefill kernel's average duration in the committed rocprofv3 kernel trace
     (profiles/prefill_kernel_trace.json) with the fraction of the HBM roofline it gives and the
     shader clock the counter run measured; None when the kernel source changed since."""
-    import hashlib
-
     path = os.path.join(ROOT, "profiles", "prefill_kernel_trace.json")
     try:
         doc = json.load(open(path))
-        src = open(os.path.join(ROOT, doc["kernel_source"]), "rb").read()
-    except (OSError, ValueError, KeyError):
+        sha = sources_sha256(doc["kernel_sources"])
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if hashlib.sha256(src).hexdigest() != doc.get("kernel_source_sha256"):
+    if sha != doc.get("kernel_sources_sha256") or doc.get("kernel") != PREFILL_KERNEL:
         return None
     us = doc["avg_us"]
     gbps = nbytes / (us / 1e6) / 1e9
@@ -362,15 +379,13 @@ def committed_trace(nbytes):
 def measured_traffic():
     """HBM bytes per prefill launch from the committed counter runs (profiles/traffic.json),
     or None when the kernel source has changed since those counters were taken."""
-    import hashlib
-
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         doc = json.load(open(path))
-        src = open(os.path.join(ROOT, doc["kernel_source"]), "rb").read()
-    except (OSError, ValueError, KeyError):
+        sha = sources_sha256(doc["kernel_sources"])
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if hashlib.sha256(src).hexdigest() != doc.get("kernel_source_sha256"):
+    if sha != doc.get("kernel_sources_sha256") or doc.get("kernel") != PREFILL_KERNEL:
         return None
     return doc.get("traffic_bytes_per_launch")
 

@@ -77,7 +77,8 @@ typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 int32_t la_abi_version(void);
 
 /*
- * Prefill (the block-wise forward pass): within each 64-token block the left product, across
+ * Prefill (the block-wise forward pass): within each block (128 tokens for bf16, 64 for fp32; see
+ * la_prefill_with_block_size) the left product, across
  * blocks the right product through the running state (digest, section 1), over a packed batch
  * of sequences delimited by cu_seqlens with the state reset at every sequence start (digest,
  * section 4, data packing).
@@ -112,9 +113,10 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
  * blocks) is exact algebra for any B, so every B gives the same result up to rounding; B only
  * trades the number of serial block steps of a scan against the size of each block's intra
  * product (4 B d + 4 d^2 FLOP per token-head).
- *   block_size  0 = the default: 64, or for bf16 storage the value of the environment variable
- *               LA_BLOCK (64 or 128; read once per process; any other value makes bf16 calls
- *               fail with LA_ERR_INVALID_ARG); la_prefill and la_prefill_ex use this default
+ *   block_size  0 = the default: 128 for bf16 storage (faster on MI355X; the environment
+ *               variable LA_BLOCK = 64 or 128 overrides it, read once per process; any other
+ *               value makes bf16 calls fail with LA_ERR_INVALID_ARG), 64 for fp32 storage;
+ *               la_prefill and la_prefill_ex use this default
  *               64 or 128 (128: bf16 storage only, else LA_ERR_UNSUPPORTED)
  * Other arguments, result and errors as la_prefill_ex, plus LA_ERR_INVALID_ARG for any other
  * block_size.  The sequence-split prefill, the backward and the fp32 path always use B = 64.

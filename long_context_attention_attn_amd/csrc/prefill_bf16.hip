@@ -53,6 +53,7 @@
 #include "la_internal.h"
 
 #include "bf16_tiles.h"
+#include "seg_lookup.h"
 
 namespace {
 
@@ -78,6 +79,11 @@ struct Cfg : RowCfg<D> {
   static constexpr int SMEM = PF_OFF + 1024;
   static_assert(STAGE < 65536, "stage offsets must fit the LDS instruction offset");
 };
+
+// LDS offset of the incoming state of a segment in the sequence-split form (see
+// split_incoming_state): after the powers table in the last stage.
+template <int D>
+constexpr int SIN_OFF() { return (NST - 1) * Cfg<D>::STAGE + 1024; }
 
 // State rows owned by state wave R (in 16-row tiles) and its first row.  Output wave r does
 // r+1 score tiles, so the low bands are larger: each SIMD's pair then does about the same
@@ -353,7 +359,7 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 // State wave r: its band of the fp32 state.  Issues the DMA of K rows 16r..16r+15; the lightest
 // state wave (r = 3) also issues the L2 prefetches.
 // ------------------------------------------------------------------------------------------
-template <int D, int R, bool SO, bool REV>
+template <int D, int R, bool SO, bool REV, bool SPLIT>
 __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const float *pw,
                                            const float *s0, float *fs, size_t sbase, int lane) {
   using C = Cfg<D>;
@@ -378,7 +384,11 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
-        kv[rt][ct][i] = s0 ? s0[sbase + (c.s0t ? (size_t)dv * D + dk : (size_t)dk * D + dv)] : 0.f;
+        if constexpr (SPLIT)  // the incoming state of the segment, formed in the prologue
+          kv[rt][ct][i] = ((const float *)(smem + SIN_OFF<D>()))[dk * CV + 16 * ct + l16];
+        else
+          kv[rt][ct][i] =
+              s0 ? s0[sbase + (c.s0t ? (size_t)dv * D + dk : (size_t)dk * D + dv)] : 0.f;
       }
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
   // Lane parts of the LDS addresses (see the output waves): state copy rows 16 ct + l16, K rows
@@ -506,15 +516,60 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   }
 }
 
+// Sequence-split form (SPLIT): one workgroup per segment slot of la_prefill_split's segment
+// numbering (seg_lookup.h); the workgroup finds its segment and forms its incoming state itself,
+// in the prologue, from the states the segment-state pass left for the earlier segments of its
+// sequence: S_in(j) = lambda^L S_in(j-1) + L(j-1), S_in(0) = the sequence's initial state (or
+// zero), L = the segment length, in fp32 with the rounding of the separate combine pass
+// (seg_decay, one fmaf per step).  The slice's S_in (D x 32 fp32) goes through LDS to the state
+// waves: it sits in the last stage after the powers table (SIN_OFF), which the first copy into
+// that stage (block 2, after the prologue barrier) overwrites.
+template <int D>
+__device__ __forceinline__ void split_incoming_state(char *smem, const float *s0,
+                                                     const float *states, const SegPos &sp,
+                                                     int H, int h, int c0, float lam_l, int tid) {
+  constexpr int E = D * CV / NTHR;  // elements per thread (8 or 4), consecutive columns
+  const int e0 = tid * E, dk = e0 / CV, col = e0 % CV;
+  const size_t off = (size_t)dk * D + c0 + col;
+  const size_t DD = (size_t)D * D;
+  float acc[E];
+  const float *src0 = s0 ? s0 + ((size_t)sp.seq * H + h) * DD + off : nullptr;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = src0 ? src0[e] : 0.f;
+  constexpr int NB = 8;  // earlier segments loaded per batch, all loads in flight together
+  for (int jb = 0; jb < sp.j; jb += NB) {
+    f32x4 buf[NB][E / 4];
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+      if (jb + x < sp.j) {
+        const float *p = states + ((size_t)(sp.first + jb + x) * H + h) * DD + off;
+#pragma unroll
+        for (int u = 0; u < E / 4; ++u) buf[x][u] = *(const f32x4 *)(p + 4 * u);
+      }
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+      if (jb + x < sp.j) {
+#pragma unroll
+        for (int u = 0; u < E / 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * u + e] = fmaf(lam_l, acc[4 * u + e], buf[x][u][e]);
+      }
+  }
+  float *sin = (float *)(smem + SIN_OFF<D>());
+#pragma unroll
+  for (int e = 0; e < E; ++e) sin[e0 + e] = acc[e];
+}
+
 // flags: bit 1 inclusive initial state (only for sequences s with incl_v[s] != 0 when incl_v is
 // given), bit 2 transposed initial state.  SO: compute only the
 // final state (q and out are not touched).  REV: reversed (anti-causal) scan.
-template <int D, bool SO, bool REV>
+template <int D, bool SO, bool REV, bool SPLIT>
 __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, __bf16 *__restrict__ out, float *__restrict__ fs, int64_t T,
-    int S, int H, int flags, const int32_t *__restrict__ incl_v) {
+    int S, int H, int flags, const int32_t *__restrict__ incl_v, int64_t seg_len,
+    const float *__restrict__ seg_states, int nslot) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -523,11 +578,20 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   float *const pw = (float *)(smem + (NST - 1) * C::STAGE);
 
   int chain, slice;
-  xcd_chain_slice(blockIdx.x, S * H * NS, NS, chain, slice);
+  xcd_chain_slice(blockIdx.x, (SPLIT ? nslot : S) * H * NS, NS, chain, slice);
   const int seq = chain / H, h = chain % H;
   Chain c;
-  const int64_t tok0 = cu ? (int64_t)cu[seq] : 0;
-  const int64_t tok1 = cu ? (int64_t)cu[seq + 1] : T;
+  int64_t tok0, tok1;
+  SegPos sp{};
+  if constexpr (SPLIT) {
+    sp = find_segment(cu, T, S, seg_len, seq);  // the same in every wave
+    if (sp.seq < 0) return;                     // an unused slot: the whole workgroup
+    tok0 = sp.tok0;
+    tok1 = sp.tok1;
+  } else {
+    tok0 = cu ? (int64_t)cu[seq] : 0;
+    tok1 = cu ? (int64_t)cu[seq + 1] : T;
+  }
   const int64_t first = (tok0 * H + h) * D;  // element offset of (tok0, h, 0)
   c.q = (const char *)(q + first);
   c.k = (const char *)(k + first);
@@ -559,17 +623,25 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     pw[tid] = (float)p;
   }
   __syncthreads();  // pw and zeroed stages visible before any DMA or read
-  const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
+  size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
+  if constexpr (SPLIT) {
+    split_incoming_state<D>(smem, s0, seg_states, sp, H, h, c.c0,
+                            seg_decay(decay[h], seg_len), tid);
+    __syncthreads();
+    // the final state is the sequence's, written by its last segment only
+    sbase = ((size_t)sp.seq * H + h) * (size_t)D * D;
+    if (sp.j != sp.count - 1) fs = nullptr;
+  }
   const int lane = tid & 63;
   switch (tid >> 6) {
     case 0: output_wave<D, 0, SO, REV>(c, smem, pw, lane); break;
     case 1: output_wave<D, 1, SO, REV>(c, smem, pw, lane); break;
     case 2: output_wave<D, 2, SO, REV>(c, smem, pw, lane); break;
     case 3: output_wave<D, 3, SO, REV>(c, smem, pw, lane); break;
-    case 4: state_wave<D, 0, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 5: state_wave<D, 1, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 6: state_wave<D, 2, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
-    default: state_wave<D, 3, SO, REV>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 4: state_wave<D, 0, SO, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 5: state_wave<D, 1, SO, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 6: state_wave<D, 2, SO, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    default: state_wave<D, 3, SO, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
   }
 }
 
@@ -579,10 +651,10 @@ hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   const long long grid = (long long)a.S * a.H * NS;
   if (grid <= 0) return hipSuccess;
   const int flags = (a.init_inclusive ? 2 : 0) | (a.init_transposed ? 4 : 0);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, SO, REV>), dim3((unsigned)grid), dim3(NTHR), 0, stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, SO, REV, false>), dim3((unsigned)grid), dim3(NTHR), 0, stream,
                      (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, a.decay,
                      a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state, a.T, a.S,
-                     a.H, flags, a.seq_incl);
+                     a.H, flags, a.seq_incl, (int64_t)0, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -596,4 +668,25 @@ hipError_t la_launch_prefill_bf16(const LaPrefillArgs &a, hipStream_t stream) {
   if (a.reverse)
     return a.D == 128 ? launch<128, false, true>(a, stream) : launch<64, false, true>(a, stream);
   return a.D == 128 ? launch<128, false, false>(a, stream) : launch<64, false, false>(a, stream);
+}
+
+hipError_t la_launch_prefill_split_bf16(const LaPrefillArgs &a, int64_t seg_len,
+                                        const float *seg_states, int32_t nslot,
+                                        hipStream_t stream) {
+  const int NS = a.D / CV;
+  const long long grid = (long long)nslot * a.H * NS;
+  if (grid <= 0) return hipSuccess;
+  if (a.D == 128)
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false, false, true>), dim3((unsigned)grid),
+                       dim3(NTHR), 0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k,
+                       (const __bf16 *)a.v, a.decay, a.cu_seqlens, a.initial_state,
+                       (__bf16 *)a.out, a.final_state, a.T, a.S, a.H, 0, nullptr, seg_len,
+                       seg_states, nslot);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, false, false, true>), dim3((unsigned)grid),
+                       dim3(NTHR), 0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k,
+                       (const __bf16 *)a.v, a.decay, a.cu_seqlens, a.initial_state,
+                       (__bf16 *)a.out, a.final_state, a.T, a.S, a.H, 0, nullptr, seg_len,
+                       seg_states, nslot);
+  return hipGetLastError();
 }

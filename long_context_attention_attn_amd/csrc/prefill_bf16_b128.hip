@@ -21,11 +21,13 @@
 //   * output wave w (w = 0..3) owns groups w and 7 - w (9 causal score tiles in all, the same for
 //     every w): S^T = K Q^T, the decay mask in registers, O^T = lambda^(j+1) KV^T Q^T + V^T P^T
 //     for both groups (the K tiles and the state copy are read once for both), and the stores.  It
-//     also copies its own Q rows and its own V rows and writes its V rows decayed,
-//     lambda^(b-1-j) V[j], for the state waves;
+//     copies its own Q rows;
 //   * state wave r holds rows 32r..32r+31 (d = 128; 16r..16r+15 at d = 64) of the fp32 state
 //     slice in MFMA accumulators for the whole sequence, KV = lambda^b KV + K^T (Lambda V) over
-//     the block's 128 tokens, copies its K rows and publishes a bf16 copy of its rows.
+//     the block's 128 tokens, and publishes a bf16 copy of its rows.  It copies K and V rows
+//     32r..32r+31 and writes those V rows decayed, lambda^(b-1-j) V[j], for the state product.
+//     (Measured: with the V copies and the decay in the output waves instead, which carry the
+//     critical path, the kernel is 0.4-0.9% slower.)
 // LDS: a two-stage ring, each stage holding a block's K and V rows, the bf16 state copy the block
 // starts from and its decayed V rows (56 KiB at d = 128), plus one Q buffer.  Only the output wave
 // that owns a Q row copies and reads it, so each output wave copies its next block's Q rows as
@@ -83,8 +85,6 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
   constexpr int GA = W, GB = NG - 1 - W;
   constexpr int NTA = GA + 1, NTB = GB + 1;            // causal score tiles of each group
   constexpr int NSA = (NTA + 1) / 2, NSB = (NTB + 1) / 2;  // 32-token k-steps of the intra product
-  constexpr int QDMA = 2 * C::QK_DMA;                 // Q copies per block (both groups)
-  constexpr int VDMA = 2;                             // V copies per block (1 KiB per group)
   constexpr int STORES = 4;                           // two groups x two 16-column tiles
   const int l16 = lane & 15, g = lane >> 4;
   const int jA = 16 * GA + l16, jB = 16 * GB + l16;  // the lane's output rows inside a block
@@ -108,23 +108,13 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       }
     }
   const float iscA = pw[jA + 1], iscB = pw[jB + 1];
-  // Decay of the lane's share of its V rows (row 16 G + lane / 4, bytes 16 (lane % 4)..+15) in a
-  // full and in the last block.
-  const int b_last = c.b_last;
-  const int vrA = 16 * GA + lane / 4, vrB = 16 * GB + lane / 4;
-  const float lvA_full = pw[BLK - 1 - vrA], lvB_full = pw[BLK - 1 - vrB];
-  const float lvA_last = vrA < b_last ? pw[b_last - 1 - vrA] : 0.f;
-  const float lvB_last = vrB < b_last ? pw[b_last - 1 - vrB] : 0.f;
 
-  // Lane offsets of the copies (Q rows of both groups, V rows of both groups) and of the stores.
+  // Lane offsets of the Q copies of both groups and of the stores.
   uint32_t qoffA[C::QK_DMA], qoffB[C::QK_DMA];
   rows_offsets<D, false>(GA, lane, rowbytes, qoffA);
   rows_offsets<D, false>(GB, lane, rowbytes, qoffB);
-  const uint32_t voffA = (uint32_t)vrA * rowbytes + 16u * ((lane % 4) ^ vswf(vrA));
-  const uint32_t voffB = (uint32_t)vrB * rowbytes + 16u * ((lane % 4) ^ vswf(vrB));
   const uint32_t ooffA = (uint32_t)jA * rowbytes + 8u * g;
   const uint32_t ooffB = (uint32_t)jB * rowbytes + 8u * g;
-  const char *vslice = c.v + 2 * c.c0;
   const uint32_t qA_lds = smem_lds + C::Q_OFF + 16 * GA * C::ROWB;
   const uint32_t qB_lds = smem_lds + C::Q_OFF + 16 * GB * C::ROWB;
 
@@ -136,19 +126,8 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
   for (int ks = 0; ks < C::KSTEPS; ++ks) kpat[ks] = (uint32_t)swz<D>(l16, 32 * ks + 8 * g);
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) vpat[ct] = (uint32_t)vswz(trow, 16 * ct + tcol);
-  const uint32_t dpatA = (uint32_t)(vrA * C::VROWB + 16 * (lane % 4));
-  const uint32_t dpatB = (uint32_t)(vrB * C::VROWB + 16 * (lane % 4));
 
-  Walk wi = walk_from<BLK, false>(c, 0), wq = walk_from<BLK, false>(c, 0),
-       ws = walk_from<BLK, false>(c, 0);
-  // V rows of the next block into the stage at st_off.
-  auto issue_v = [&](uint32_t st_off) {
-    const Span sp = span_at<false>(c, wi);
-    advance<false>(c, wi);
-    const uint32_t st = smem_lds + st_off + C::V_OFF;
-    dma16x2(rsrc(vslice + sp.off, sp.bytes), voffA, voffB, st + 16 * GA * C::VROWB,
-            st + 16 * GB * C::VROWB);
-  };
+  Walk wq = walk_from<BLK, false>(c, 0), ws = walk_from<BLK, false>(c, 0);
   // Q rows of the next block into the Q buffer.
   auto issue_q = [&]() {
     const Span sp = span_at<false>(c, wq);
@@ -156,29 +135,15 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
     dma_rows<D, false>(c.q, sp, qoffA, qA_lds);
     dma_rows<D, false>(c.q, sp, qoffB, qB_lds);
   };
-  // This wave's V rows of block blk (landed in the stage at st_off), decayed, into the same stage.
-  auto decay_v = [&](int blk, uint32_t st_off) {
-    const bool last = blk == c.nb - 1;
-    uint32_t da = dpatA + st_off, db = dpatB + st_off;
-    asm volatile("" : "+v"(da), "+v"(db));
-    const bf16x8 xa = *(const bf16x8 *)(smem + da + C::V_OFF);
-    const bf16x8 xb = *(const bf16x8 *)(smem + db + C::V_OFF);
-    *(bf16x8 *)(smem + da + C::LV_OFF) = scale8(xa, last ? lvA_last : lvA_full);
-    *(bf16x8 *)(smem + db + C::LV_OFF) = scale8(xb, last ? lvB_last : lvB_full);
-  };
-
-  issue_v(0);
   issue_q();
   wait_vm<0>();
-  decay_v(0, 0);
   lds_barrier();  // block 0, its decayed V and the initial state copy visible to all waves
 
   uint32_t s_cur = 0, s_nxt = C::STAGE;
   for (int i = 0; i < c.nb; ++i) {
-    issue_v(s_nxt);  // block i + 1, into the stage block i - 1 used
-    // Own Q rows of block i landed: since their copy this wave issued the previous block's
-    // stores and the copy just above.
-    wait_vm<STORES + VDMA>();
+    // Own Q rows of block i landed: since their copy this wave issued only the previous
+    // block's stores.
+    wait_vm<STORES>();
     bf16x8 qa[C::KSTEPS], qb[C::KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
@@ -296,10 +261,6 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       }
     }
     advance<false>(c, ws);
-    // Own V rows of block i + 1 landed: since their copy this wave issued the Q copies and the
-    // stores of this step.
-    wait_vm<QDMA + STORES>();
-    decay_v(i + 1, s_nxt);
     lds_barrier();
     const uint32_t so = s_cur;
     s_cur = s_nxt;
@@ -387,13 +348,44 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
                   rsrc(c.v + sp.off, sp.bytes), pfoff, smem_lds + C::PF_OFF);
     }
   };
+  // V rows 32R..32R+31 (two 1 KiB copies) and their decayed copy lambda^(b-1-j) V[j], which the
+  // state product reads.
+  const int vr0 = 32 * R + lane / 4, vr1 = vr0 + 16;
+  const uint32_t voff0 = (uint32_t)vr0 * c.rowbytes + 16u * ((lane % 4) ^ vswf(vr0));
+  const uint32_t voff1 = (uint32_t)vr1 * c.rowbytes + 16u * ((lane % 4) ^ vswf(vr1)) - 1024u;
+  const float lv0_full = pw[BLK - 1 - vr0], lv1_full = pw[BLK - 1 - vr1];
+  const float lv0_last = vr0 < b_last ? pw[b_last - 1 - vr0] : 0.f;
+  const float lv1_last = vr1 < b_last ? pw[b_last - 1 - vr1] : 0.f;
+  const uint32_t dpat = (uint32_t)(vr0 * C::VROWB + 16 * (lane % 4));
+  const char *vslice = c.v + 2 * c.c0;
+  Walk wv = walk_from<BLK, false>(c, 0);
+  auto issue_v = [&](uint32_t st_off) {
+    const Span sp = span_at<false>(c, wv);
+    advance<false>(c, wv);
+    dma_kib2(rsrc(vslice + sp.off, sp.bytes), voff0, voff1,
+             smem_lds + st_off + C::V_OFF + 32 * R * C::VROWB);
+  };
+  // The decayed copy of the rows of block blk (landed in the stage at st_off), in that stage.
+  auto decay_v = [&](int blk, uint32_t st_off) {
+    const bool last = blk == c.nb - 1;
+    uint32_t d = dpat + st_off;
+    asm volatile("" : "+v"(d));
+    const bf16x8 x0 = *(const bf16x8 *)(smem + d + C::V_OFF);
+    const bf16x8 x1 = *(const bf16x8 *)(smem + d + C::V_OFF + 16 * C::VROWB);
+    *(bf16x8 *)(smem + d + C::LV_OFF) = scale8(x0, last ? lv0_last : lv0_full);
+    *(bf16x8 *)(smem + d + C::LV_OFF + 16 * C::VROWB) = scale8(x1, last ? lv1_last : lv1_full);
+  };
   issue_k(0);
+  issue_v(0);
   prefetch();  // block 1
+  wait_vm<PF ? PF_DMA : 0>();
+  decay_v(0, 0);
   wait_vm_barrier<PF ? PF_DMA : 0>();
 
   uint32_t s_cur = 0, s_nxt = C::STAGE;
   for (int i = 0; i < c.nb; ++i) {
     issue_k(s_nxt);  // block i + 1, into the stage block i - 1 used
+    issue_v(s_nxt);
     prefetch();      // block i + 2
     uint32_t kb[RT], vb[2];
 #pragma unroll
@@ -430,7 +422,9 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
       }
     }
     write_kvx(s_nxt);
-    // Own K rows of block i + 1 landed (only the prefetch was issued after them).
+    // Own K and V rows of block i + 1 landed (only the prefetch was issued after them).
+    wait_vm<PF ? PF_DMA : 0>();
+    decay_v(i + 1, s_nxt);
     wait_vm_barrier<PF ? PF_DMA : 0>();
     const uint32_t so = s_cur;
     s_cur = s_nxt;

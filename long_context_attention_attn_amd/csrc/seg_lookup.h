@@ -1,0 +1,85 @@
+// seg_lookup.h -- where one segment of the sequence-split prefill lies, found on the device.
+//
+// The split prefill cuts every sequence of a packed batch into segments of seg_len tokens (the
+// last one shorter) and numbers them sequence by sequence: slot g is segment j of sequence s
+// when g = first(s) + j, first(s) = sum over earlier sequences of ceil(n / seg_len).  A kernel
+// that has one workgroup per slot finds its segment with this one-wave scan over cu_seqlens
+// instead of reading a table another launch built.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct SegPos {
+  int seq;             // the sequence, or -1 for an unused slot (past the last segment)
+  int j;               // the segment's index within its sequence
+  int first;           // slot of the sequence's first segment
+  int count;           // segments of the sequence
+  int64_t tok0, tok1;  // the segment's tokens [tok0, tok1)
+};
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Called by all 64 lanes of a wave with the same arguments; every lane gets the same result,
+// as wave-uniform (scalar) values.  cu = nullptr means one sequence of T tokens.  Empty
+// sequences have no segments.
+__device__ inline SegPos find_segment(const int32_t *cu, int64_t T, int S, int64_t seg_len, int g) {
+  const int lane = threadIdx.x & 63;
+  SegPos r{-1, 0, 0, 0, 0, 0};
+  int before = 0;  // segments of the sequences before this chunk of 64
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    int64_t t0 = 0, t1 = 0;
+    if (s < S) {
+      t0 = cu ? (int64_t)cu[s] : 0;
+      t1 = cu ? (int64_t)cu[s + 1] : T;
+    }
+    const int64_t n = t1 > t0 ? t1 - t0 : 0;
+    const int cnt = (int)((n + seg_len - 1) / seg_len);
+    int incl = cnt;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int x = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += x;
+    }
+    const int excl = incl - cnt;
+    const unsigned long long hit = __ballot(s < S && g >= before + excl && g < before + incl);
+    if (hit) {
+      const int l = __ffsll(hit) - 1;
+      r.seq = base + l;
+      r.first = before + __shfl(excl, l, 64);
+      r.count = __shfl(cnt, l, 64);
+      r.j = g - r.first;
+      const int64_t s0 = cu ? (int64_t)cu[r.seq] : 0, s1 = cu ? (int64_t)cu[r.seq + 1] : T;
+      r.tok0 = s0 + (int64_t)r.j * seg_len;
+      r.tok1 = r.tok0 + seg_len < s1 ? r.tok0 + seg_len : s1;
+      r.seq = uniform(r.seq);
+      r.j = uniform(r.j);
+      r.first = uniform(r.first);
+      r.count = uniform(r.count);
+      r.tok0 = uniform64(r.tok0);
+      r.tok1 = uniform64(r.tok1);
+      return r;
+    }
+    before += __shfl(incl, 63, 64);
+  }
+  return r;
+}
+
+// lambda^m in double by binary powering, rounded to float (exact for lambda in {0, 1}; 0^0 = 1):
+// the decay of a state across a segment of m tokens.  The combine and the segment prefill's
+// own combine use this one definition, so both round the same way.
+__device__ __forceinline__ float seg_decay(float lam, int64_t m) {
+  double r = 1.0, b = (double)lam;
+  while (m > 0) {
+    if (m & 1) r *= b;
+    b *= b;
+    m >>= 1;
+  }
+  return (float)r;
+}

@@ -24,6 +24,7 @@
 // segments from the last to the first (the combine's reversed-inclusive mode), and the segment
 // table flags the last segment of every sequence, the one that starts from the inclusive state.
 #include "la_internal.h"
+#include "seg_lookup.h"
 
 namespace {
 
@@ -84,17 +85,6 @@ __global__ __launch_bounds__(TBL_THREADS) void seg_table_kernel(
   }
 }
 
-// lambda^m in double by binary powering (exact for lambda in {0, 1}; 0^0 = 1).
-__device__ __forceinline__ float powi(float lam, int64_t m) {
-  double r = 1.0, b = (double)lam;
-  while (m > 0) {
-    if (m & 1) r *= b;
-    b *= b;
-    m >>= 1;
-  }
-  return (float)r;
-}
-
 // Combine, in place: st[g] holds L of segment g on entry and S_in of segment g on exit.  One
 // thread per state element (a, b) of one (sequence, head); it walks the sequence's segments in
 // scan order.  final_state[s][h] (if given) receives the state after the last segment: the
@@ -124,7 +114,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float l = *p;
     *p = carry;
     const int64_t m = (int64_t)seg_cu[g + 1] - seg_cu[g] - (rinc && x == 0 ? 1 : 0);
-    carry = fmaf(powi(lam, m), carry, l);
+    carry = fmaf(seg_decay(lam, m), carry, l);
   }
   if (fs) fs[(size_t)sh * DD + e] = rinc && n > 0 ? lam * carry : carry;
 }
@@ -200,10 +190,22 @@ __device__ __forceinline__ bf16x4 tr_read4(const char *p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int D>
+// The segment table is either read (cu = segment starts, FUSED = false) or found by the
+// workgroup itself (FUSED: cu = the sequences' cu_seqlens, slot = segment as in seg_lookup.h);
+// the fused form also writes the final states of empty sequences (their initial states, or
+// zeros), the one thing the segment prefill that follows cannot do.
+struct FusedSeg {
+  int64_t T;
+  int S;
+  int64_t seg_len;
+  const float *s0;  // [S][H][D][D] initial states or nullptr
+  float *fs_seq;    // [S][H][D][D] final states or nullptr
+};
+
+template <int D, bool FUSED>
 __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, const float *__restrict__ decay,
-    const int32_t *__restrict__ cu, float *__restrict__ fs, int H, int rev) {
+    const int32_t *__restrict__ cu, float *__restrict__ fs, int H, int rev, FusedSeg fz) {
   using C = SsCfg<D>;
   constexpr int NS = D / SS_CV;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -227,11 +229,32 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
     slice = pos % NS;
   }
   const int seg = chain / H, h = chain % H;
-  const int64_t tok0 = cu[seg], tok1 = cu[seg + 1];
+  int64_t tok0, tok1;
+  if constexpr (FUSED) {
+    const SegPos sp = find_segment(cu, fz.T, fz.S, fz.seg_len, seg);
+    tok0 = sp.seq >= 0 ? sp.tok0 : 0;
+    tok1 = sp.seq >= 0 ? sp.tok1 : 0;
+  } else {
+    tok0 = cu[seg];
+    tok1 = cu[seg + 1];
+  }
   const int n = tok1 > tok0 ? (int)(tok1 - tok0) : 0;
   const int64_t rowstride = (int64_t)H * D;
   const int c0 = slice * SS_CV;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  if constexpr (FUSED) {
+    // Sequence `seg` (slots outnumber sequences), if empty: its final state is its initial one.
+    if (fz.fs_seq && seg < fz.S) {
+      const int64_t a = cu ? (int64_t)cu[seg] : 0, b = cu ? (int64_t)cu[seg + 1] : fz.T;
+      if (b <= a) {
+        const size_t base = ((size_t)seg * H + h) * D * D + c0;
+        for (int e = tid; e < D * SS_CV; e += SS_WAVES * 64) {
+          const size_t off = base + (size_t)(e / SS_CV) * D + e % SS_CV;
+          fz.fs_seq[off] = fz.s0 ? fz.s0[off] : 0.f;
+        }
+      }
+    }
+  }
   const double lam = (double)decay[h];
 
   // Buffer descriptors over the segment's rows of head h (K) and of the value slice (V): byte
@@ -408,13 +431,33 @@ hipError_t la_launch_segment_states_bf16(const LaPrefillArgs &a, int64_t max_len
   // otherwise the block scan's state-only form gives the same states.
   if ((max_len + 2 * SS_CH) * (int64_t)a.H * a.D * 2 >= (int64_t)1 << 31)
     return la_launch_prefill_bf16(a, stream);
+  const FusedSeg none{};
   if (a.D == 128)
-    hipLaunchKernelGGL(segment_states_kernel<128>, dim3((unsigned)grid), dim3(SS_WAVES * 64), 0,
-                       stream, (const __bf16 *)a.k, (const __bf16 *)a.v, a.decay, a.cu_seqlens,
-                       a.final_state, a.H, (int)a.reverse);
+    hipLaunchKernelGGL((segment_states_kernel<128, false>), dim3((unsigned)grid),
+                       dim3(SS_WAVES * 64), 0, stream, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                       a.decay, a.cu_seqlens, a.final_state, a.H, (int)a.reverse, none);
   else
-    hipLaunchKernelGGL(segment_states_kernel<64>, dim3((unsigned)grid), dim3(SS_WAVES * 64), 0,
-                       stream, (const __bf16 *)a.k, (const __bf16 *)a.v, a.decay, a.cu_seqlens,
-                       a.final_state, a.H, (int)a.reverse);
+    hipLaunchKernelGGL((segment_states_kernel<64, false>), dim3((unsigned)grid),
+                       dim3(SS_WAVES * 64), 0, stream, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                       a.decay, a.cu_seqlens, a.final_state, a.H, (int)a.reverse, none);
+  return hipGetLastError();
+}
+
+hipError_t la_launch_segment_states_fused_bf16(const int32_t *cu_seqlens, int64_t T, int32_t S,
+                                               int64_t seg_len, int32_t cap, const void *k,
+                                               const void *v, const float *decay, int32_t H,
+                                               int32_t D, float *states, const float *s0,
+                                               float *fs, hipStream_t stream) {
+  const long long grid = (long long)cap * H * (D / SS_CV);
+  if (grid <= 0) return hipSuccess;
+  const FusedSeg fz{T, S, seg_len, s0, fs};
+  if (D == 128)
+    hipLaunchKernelGGL((segment_states_kernel<128, true>), dim3((unsigned)grid),
+                       dim3(SS_WAVES * 64), 0, stream, (const __bf16 *)k, (const __bf16 *)v,
+                       decay, cu_seqlens, states, H, 0, fz);
+  else
+    hipLaunchKernelGGL((segment_states_kernel<64, true>), dim3((unsigned)grid),
+                       dim3(SS_WAVES * 64), 0, stream, (const __bf16 *)k, (const __bf16 *)v,
+                       decay, cu_seqlens, states, H, 0, fz);
   return hipGetLastError();
 }

@@ -50,14 +50,16 @@ def test_block_sizes_match_oracle_and_each_other(D, with_init):
     assert state_errors(res[128][1], res[64][1]).max() <= BF16_TOL
 
 
-def test_default_block_is_64_bitwise():
+def test_default_block_is_128_for_bf16_bitwise():
     banner("default block size")
     cu = synth.cu_from_lengths([300, 65])
     q, k, v = synth.qkv(365, 2, 128, torch.bfloat16, seed=43)
     decay = synth.decay_geometric(2, 0.9, 0.999)
     o0, s0 = _prefill(q, k, v, decay, cu)
-    o1, s1 = _prefill(q, k, v, decay, cu, block_size=64)
+    o1, s1 = _prefill(q, k, v, decay, cu, block_size=128)
+    o2, _ = _prefill(q, k, v, decay, cu, block_size=64)
     assert torch.equal(o0, o1) and torch.equal(s0, s1)
+    assert not torch.equal(o0, o2)  # the 64-token kernel rounds differently
 
 
 def test_block128_deterministic_and_causal():

@@ -153,3 +153,37 @@ def test_split_suggestion_uses_the_device():
     oa, fa = _split_prefill(q, k, v, decay, split="auto")
     ob, fb = _split_prefill(q, k, v, decay, split=seg)
     assert torch.equal(oa, ob) and torch.equal(fa, fb)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_two_launch_path_packed(D):
+    """The bf16 split in two launches (segments found on the device, incoming states formed in
+    the segment prefill's prologue): packed sequences with empty ones, initial states, up to 16
+    segments per sequence, against the oracle; bitwise deterministic."""
+    lengths = [1000, 0, 1, 64, 2049, 0, 700]
+    H = 3
+    banner("split two-launch D=%d lengths=%s" % (D, lengths))
+    d = dev()
+    cu = synth.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=61)
+    decay = torch.tensor([0.0, 0.93, 1.0], dtype=torch.float32)
+    init = synth.random_state(len(lengths), H, D, seed=62, scale=0.1)
+    seg = 4  # 256-token segments: ceil(T / 256) = 16, within the two-launch path's bound
+    assert (T + 64 * seg - 1) // (64 * seg) <= 16
+    outs = []
+    for _ in range(2):
+        out, fs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d), cu.to(d),
+                             initial_state=init.to(d), split=seg)
+        torch.cuda.synchronize()
+        outs.append((out.cpu(), fs.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    ref = oracle.quadratic(q, k, v, decay, cu, init_state=init)
+    ref_s = oracle.final_state(k, v, decay, cu, init_state=init)
+    e = slice_errors(to_np(outs[0][0]), ref, cu).max()
+    es = state_errors(to_np(outs[0][1]), ref_s).max()
+    print("two-launch split D=%d: out %.2e state %.2e" % (D, e, es))
+    assert e <= BF16_TOL and es <= BF16_TOL
+    # empty sequences keep their initial state exactly
+    for s in (1, 5):
+        assert torch.equal(outs[0][1][s], init[s])
