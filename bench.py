@@ -44,6 +44,10 @@ PREFILL_SOURCES = ("long_context_attention_attn_amd/csrc/prefill_bf16_b128.hip",
                    "long_context_attention_attn_amd/csrc/bf16_tiles.h")
 
 
+EXTRA_LEGS = ("varlen_prefill", "long_prefill", "few_chain_prefill", "backward",
+              "few_chain_backward", "decode_tokens", "fp32_prefill", "measured_peaks")
+
+
 def prefill_flop(T, H, D, B=BLOCK_FLOP_B):
     # per token-head: intra 4*B*D (QK^T and PV over full BxB tiles) + inter 2*D^2 + state 2*D^2
     return T * H * (4 * B * D + 4 * D * D)
@@ -67,11 +71,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra legs timed after the K steps")
+    ap.add_argument("--extras", default=",".join(EXTRA_LEGS),
+                    help="comma-separated extra legs to run (default: all of %s)"
+                         % ", ".join(EXTRA_LEGS))
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, time a plain device-to-device copy of this "
                          "many MiB (K times); used to calibrate HBM byte counters")
     args = ap.parse_args()
+    chosen = [x for x in args.extras.split(",") if x]
+    for name in chosen:
+        if name not in EXTRA_LEGS:
+            print("unknown extra leg %r (known: %s)" % (name, ", ".join(EXTRA_LEGS)),
+                  file=sys.stderr)
+            sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and there "
               "is no multi-GPU path (heads and sequences would shard with no communication).  "
@@ -186,14 +199,19 @@ def main():
 
     if not args.no_extras:
         del q, k, v, out
-        result["varlen_prefill"] = long_prefill_leg("varlen_16", dev)
-        result["long_prefill"] = long_prefill_leg("prefill_1m", dev)
-        result["few_chain_prefill"] = few_chain_prefill(dev)
-        result["backward"] = backward_leg(wl, dev)
-        result["few_chain_backward"] = few_chain_backward(dev)
-        result["decode_tokens"] = decode_tokens_leg(dev)
-        result["fp32_prefill"] = fp32_prefill_leg(dev)
-        result["measured_peaks"] = measured_peaks(dev)
+        legs = {
+            "varlen_prefill": lambda: long_prefill_leg("varlen_16", dev),
+            "long_prefill": lambda: long_prefill_leg("prefill_1m", dev),
+            "few_chain_prefill": lambda: few_chain_prefill(dev),
+            "backward": lambda: backward_leg(wl, dev),
+            "few_chain_backward": lambda: few_chain_backward(dev),
+            "decode_tokens": lambda: decode_tokens_leg(dev),
+            "fp32_prefill": lambda: fp32_prefill_leg(dev),
+            "measured_peaks": lambda: measured_peaks(dev),
+        }
+        for name in EXTRA_LEGS:
+            if name in chosen:
+                result[name] = legs[name]()
     if not args.no_cpu_baseline:
         q, k, v = wl.inputs(device=dev)
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, args.cpu_sample_tokens, tokens_per_step)

@@ -70,6 +70,10 @@ hipError_t la_launch_segment_states_fused_bf16(const int32_t *cu_seqlens, int64_
 hipError_t la_launch_prefill_split_bf16(const LaPrefillArgs &a, int64_t seg_len,
                                         const float *seg_states, int32_t nslot,
                                         hipStream_t stream);
+// The same with 128-token blocks (seg_len a multiple of 128).
+hipError_t la_launch_prefill_split_bf16_b128(const LaPrefillArgs &a, int64_t seg_len,
+                                             const float *seg_states, int32_t nslot,
+                                             hipStream_t stream);
 // s0_transposed: read s0[s][h][b][a] as element [a][b].  reverse_inclusive: walk each sequence's
 // segments from last to first (a reversed scan), the first one counting s0 as inclusive.
 hipError_t la_launch_combine(const float *decay, const int32_t *seg_cu, const int32_t *seq_seg0,

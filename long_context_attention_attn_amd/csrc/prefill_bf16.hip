@@ -524,42 +524,6 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
 // (seg_decay, one fmaf per step).  The slice's S_in (D x 32 fp32) goes through LDS to the state
 // waves: it sits in the last stage after the powers table (SIN_OFF), which the first copy into
 // that stage (block 2, after the prologue barrier) overwrites.
-template <int D>
-__device__ __forceinline__ void split_incoming_state(char *smem, const float *s0,
-                                                     const float *states, const SegPos &sp,
-                                                     int H, int h, int c0, float lam_l, int tid) {
-  constexpr int E = D * CV / NTHR;  // elements per thread (8 or 4), consecutive columns
-  const int e0 = tid * E, dk = e0 / CV, col = e0 % CV;
-  const size_t off = (size_t)dk * D + c0 + col;
-  const size_t DD = (size_t)D * D;
-  float acc[E];
-  const float *src0 = s0 ? s0 + ((size_t)sp.seq * H + h) * DD + off : nullptr;
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = src0 ? src0[e] : 0.f;
-  constexpr int NB = 8;  // earlier segments loaded per batch, all loads in flight together
-  for (int jb = 0; jb < sp.j; jb += NB) {
-    f32x4 buf[NB][E / 4];
-#pragma unroll
-    for (int x = 0; x < NB; ++x)
-      if (jb + x < sp.j) {
-        const float *p = states + ((size_t)(sp.first + jb + x) * H + h) * DD + off;
-#pragma unroll
-        for (int u = 0; u < E / 4; ++u) buf[x][u] = *(const f32x4 *)(p + 4 * u);
-      }
-#pragma unroll
-    for (int x = 0; x < NB; ++x)
-      if (jb + x < sp.j) {
-#pragma unroll
-        for (int u = 0; u < E / 4; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[4 * u + e] = fmaf(lam_l, acc[4 * u + e], buf[x][u][e]);
-      }
-  }
-  float *sin = (float *)(smem + SIN_OFF<D>());
-#pragma unroll
-  for (int e = 0; e < E; ++e) sin[e0 + e] = acc[e];
-}
-
 // flags: bit 1 inclusive initial state (only for sequences s with incl_v[s] != 0 when incl_v is
 // given), bit 2 transposed initial state.  SO: compute only the
 // final state (q and out are not touched).  REV: reversed (anti-causal) scan.
@@ -625,8 +589,8 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   __syncthreads();  // pw and zeroed stages visible before any DMA or read
   size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   if constexpr (SPLIT) {
-    split_incoming_state<D>(smem, s0, seg_states, sp, H, h, c.c0,
-                            seg_decay(decay[h], seg_len), tid);
+    split_incoming_state<D, CV, NTHR>((float *)(smem + SIN_OFF<D>()), s0, seg_states, sp, H, h,
+                                      c.c0, seg_decay(decay[h], seg_len), tid);
     __syncthreads();
     // the final state is the sequence's, written by its last segment only
     sbase = ((size_t)sp.seq * H + h) * (size_t)D * D;

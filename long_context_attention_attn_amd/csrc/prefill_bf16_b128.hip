@@ -36,6 +36,7 @@
 // into L2 during step i, so those copies hit L2.  One barrier per block.
 #include "la_internal.h"
 #include "bf16_tiles.h"
+#include "seg_lookup.h"
 
 namespace {
 
@@ -59,6 +60,14 @@ struct Cfg : RowCfg<D> {
   static_assert(STAGE < 65536 && BLK * ROWB < 65536,
                 "stage and Q offsets must fit the LDS instruction offset");
 };
+
+// Sequence-split form (SPLIT): one workgroup per segment slot of la_prefill_split's segment
+// numbering (seg_lookup.h), which finds its segment and forms its incoming state in the
+// prologue from the states the segment-state pass left (split_incoming_state).  The slice's
+// incoming state (D x 32 fp32) reaches the state waves through LDS, after the powers table in
+// stage 1, which the first copies into that stage (step 0, after the prologue barrier) overwrite.
+template <int D>
+constexpr int SIN_OFF() { return Cfg<D>::STAGE + 1024; }
 
 // State rows of state wave r: 16-row tiles [TILES r, TILES (r + 1)).
 template <int D>
@@ -273,7 +282,7 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 // State wave R: state rows [16 RT R, 16 RT (R + 1)) of the slice.  Copies K rows
 // [BLK/4 R, BLK/4 (R + 1)); the last state wave also issues the L2 prefetches.
 // ------------------------------------------------------------------------------------------
-template <int D, int R>
+template <int D, int R, bool SPLIT>
 __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const float *pw,
                                            const float *s0, float *fs, size_t sbase, int lane) {
   using C = Cfg<D>;
@@ -293,7 +302,10 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
-        kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
+        if constexpr (SPLIT)  // the incoming state of the segment, formed in the prologue
+          kv[rt][ct][i] = ((const float *)(smem + SIN_OFF<D>()))[dk * CV + 16 * ct + l16];
+        else
+          kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
       }
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
   uint32_t xpat[RT], kpat[RT], vpat[2];
@@ -445,12 +457,12 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   }
 }
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, __bf16 *__restrict__ out, float *__restrict__ fs, int64_t T,
-    int S, int H) {
+    int S, int H, int64_t seg_len, const float *__restrict__ seg_states, int nslot) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -459,11 +471,20 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
   float *const pw = (float *)(smem + C::STAGE);
 
   int chain, slice;
-  xcd_chain_slice(blockIdx.x, S * H * NS, NS, chain, slice);
+  xcd_chain_slice(blockIdx.x, (SPLIT ? nslot : S) * H * NS, NS, chain, slice);
   const int seq = chain / H, h = chain % H;
   Chain c;
-  const int64_t tok0 = cu ? (int64_t)cu[seq] : 0;
-  const int64_t tok1 = cu ? (int64_t)cu[seq + 1] : T;
+  int64_t tok0, tok1;
+  SegPos sp{};
+  if constexpr (SPLIT) {
+    sp = find_segment(cu, T, S, seg_len, seq);  // the same in every wave
+    if (sp.seq < 0) return;                     // an unused slot: the whole workgroup
+    tok0 = sp.tok0;
+    tok1 = sp.tok1;
+  } else {
+    tok0 = cu ? (int64_t)cu[seq] : 0;
+    tok1 = cu ? (int64_t)cu[seq + 1] : T;
+  }
   const int64_t first = (tok0 * H + h) * D;  // element offset of (tok0, h, 0)
   c.q = (const char *)(q + first);
   c.k = (const char *)(k + first);
@@ -495,17 +516,25 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
     pw[tid] = (float)p;
   }
   __syncthreads();  // pw and zeroed buffers visible before any copy or read
-  const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
+  size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
+  if constexpr (SPLIT) {
+    split_incoming_state<D, CV, NTHR>((float *)(smem + SIN_OFF<D>()), s0, seg_states, sp, H, h,
+                                      c.c0, seg_decay(decay[h], seg_len), tid);
+    __syncthreads();
+    // the final state is the sequence's, written by its last segment only
+    sbase = ((size_t)sp.seq * H + h) * (size_t)D * D;
+    if (sp.j != sp.count - 1) fs = nullptr;
+  }
   const int lane = tid & 63;
   switch (tid >> 6) {
     case 0: output_wave<D, 0>(c, smem, pw, lane); break;
     case 1: output_wave<D, 1>(c, smem, pw, lane); break;
     case 2: output_wave<D, 2>(c, smem, pw, lane); break;
     case 3: output_wave<D, 3>(c, smem, pw, lane); break;
-    case 4: state_wave<D, 0>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 5: state_wave<D, 1>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 6: state_wave<D, 2>(c, smem, pw, s0, fs, sbase, lane); break;
-    default: state_wave<D, 3>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 4: state_wave<D, 0, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 5: state_wave<D, 1, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 6: state_wave<D, 2, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    default: state_wave<D, 3, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
   }
 }
 
@@ -514,10 +543,23 @@ hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   const int NS = D / CV;
   const long long grid = (long long)a.S * a.H * NS;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_bf16_b128_kernel<D>, dim3((unsigned)grid), dim3(NTHR), 0, stream,
-                     (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, a.decay,
-                     a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state, a.T, a.S,
-                     a.H);
+  hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, false>), dim3((unsigned)grid), dim3(NTHR), 0,
+                     stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                     a.decay, a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state,
+                     a.T, a.S, a.H, (int64_t)0, nullptr, 0);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split(const LaPrefillArgs &a, int64_t seg_len, const float *seg_states,
+                        int32_t nslot, hipStream_t stream) {
+  const int NS = D / CV;
+  const long long grid = (long long)nslot * a.H * NS;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, true>), dim3((unsigned)grid), dim3(NTHR), 0,
+                     stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                     a.decay, a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state,
+                     a.T, a.S, a.H, seg_len, seg_states, nslot);
   return hipGetLastError();
 }
 
@@ -527,4 +569,12 @@ hipError_t la_launch_prefill_bf16_b128(const LaPrefillArgs &a, hipStream_t strea
   if (a.reverse || a.state_only || a.init_inclusive || a.init_transposed || a.seq_incl)
     return hipErrorInvalidValue;  // forward scans only
   return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
+}
+
+hipError_t la_launch_prefill_split_bf16_b128(const LaPrefillArgs &a, int64_t seg_len,
+                                             const float *seg_states, int32_t nslot,
+                                             hipStream_t stream) {
+  if (seg_len % BLK != 0) return hipErrorInvalidValue;  // segments of whole 128-token blocks
+  return a.D == 128 ? launch_split<128>(a, seg_len, seg_states, nslot, stream)
+                    : launch_split<64>(a, seg_len, seg_states, nslot, stream);
 }

@@ -83,3 +83,46 @@ __device__ __forceinline__ float seg_decay(float lam, int64_t m) {
   }
   return (float)r;
 }
+
+// The incoming state S_in of a segment's CV-column value slice, formed by the workgroup that
+// prefills the segment (NTHR threads, D * CV / NTHR consecutive elements each) from the states
+// an earlier pass left for the earlier segments of its sequence:
+//   S_in(0) = the sequence's initial state (or zero),  S_in(j) = lambda^L S_in(j-1) + L(j-1),
+// in fp32 with one fmaf per step (the rounding of a separate combine pass over the same states).
+// s0: [S][H][D][D] or nullptr; states: [slots][H][D][D]; sin: the [D][CV] fp32 result (LDS).
+template <int D, int CV, int NTHR>
+__device__ __forceinline__ void split_incoming_state(float *sin, const float *s0,
+                                                     const float *states, const SegPos &sp,
+                                                     int H, int h, int c0, float lam_l, int tid) {
+  typedef __attribute__((ext_vector_type(4))) float f4;
+  constexpr int E = D * CV / NTHR;  // elements per thread, consecutive columns
+  static_assert(E % 4 == 0 && CV % E == 0, "whole 16-byte pieces of one row per thread");
+  const int e0 = tid * E, dk = e0 / CV, col = e0 % CV;
+  const size_t off = (size_t)dk * D + c0 + col;
+  const size_t DD = (size_t)D * D;
+  float acc[E];
+  const float *src0 = s0 ? s0 + ((size_t)sp.seq * H + h) * DD + off : nullptr;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = src0 ? src0[e] : 0.f;
+  constexpr int NB = 8;  // earlier segments loaded per batch, all loads in flight together
+  for (int jb = 0; jb < sp.j; jb += NB) {
+    f4 buf[NB][E / 4];
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+      if (jb + x < sp.j) {
+        const float *p = states + ((size_t)(sp.first + jb + x) * H + h) * DD + off;
+#pragma unroll
+        for (int u = 0; u < E / 4; ++u) buf[x][u] = *(const f4 *)(p + 4 * u);
+      }
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+      if (jb + x < sp.j) {
+#pragma unroll
+        for (int u = 0; u < E / 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * u + e] = fmaf(lam_l, acc[4 * u + e], buf[x][u][e]);
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) sin[e0 + e] = acc[e];
+}

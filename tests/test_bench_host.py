@@ -35,3 +35,10 @@ def test_prefill_bytes():
 def test_decode_bytes():
     # fp32 state read + write, bf16 q, k, v, o, fp32 decay: 2,164,261,120 B at 256 x 64 x 128
     assert bench.decode_bytes(256, 64, 128) == 2164261120
+
+
+def test_unknown_extra_leg_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--extras", "nope"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "unknown extra leg" in r.stderr and "fp32_prefill" in r.stderr

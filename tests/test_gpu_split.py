@@ -187,3 +187,28 @@ def test_split_two_launch_path_packed(D):
     # empty sequences keep their initial state exactly
     for s in (1, 5):
         assert torch.equal(outs[0][1][s], init[s])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("seg_blocks", [64, 66])
+def test_split_long_segment_kernels(D, seg_blocks):
+    """Segments of 4,096 tokens (whole 128-token blocks: the 128-token segment prefill) and of
+    4,224 tokens (the 64-token one) over packed sequences with an empty one and a partial last
+    block, from initial states, against the recurrent form."""
+    lengths = [9000, 0, 4096, 5000, 129]
+    H = 2
+    banner("split long segment kernels D=%d seg_blocks=%d" % (D, seg_blocks))
+    d = dev()
+    cu = synth.cu_from_lengths(lengths)
+    q, k, v = synth.qkv(int(cu[-1]), H, D, torch.bfloat16, seed=63)
+    decay = torch.tensor([0.95, 0.9999], dtype=torch.float32)
+    init = synth.random_state(len(lengths), H, D, seed=64, scale=0.1)
+    out, fs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d), cu.to(d),
+                         initial_state=init.to(d), split=seg_blocks)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(q, k, v, decay, cu, init_state=init)
+    e = slice_errors(to_np(out), ref, cu).max()
+    es = state_errors(to_np(fs), ref_s).max()
+    print("long segments D=%d seg=%d: out %.2e state %.2e" % (D, seg_blocks, e, es))
+    assert e <= BF16_TOL and es <= BF16_TOL
+    assert torch.equal(fs.cpu()[1], init[1])
