@@ -289,28 +289,30 @@ def decode_tokens_leg(dev, iters=20, warmup=3):
 
 
 def few_chain_prefill(dev, iters=20, warmup=3):
-    """Prefill shapes with few (sequence, head) chains -- 8,192 x 8 heads and 65,536 x 8 heads
-    (one device's share of the 64-head layer under 8-way head sharding) -- timed with the plain
-    scan and with the sequence split the library suggests."""
+    """Prefill shapes with fewer (sequence, head, 32-column slice) chains than compute units --
+    8,192 x 8 heads and 65,536 x 8 heads (one device's share of the 64-head layer under 8-way head
+    sharding) at d = 128, and the 64-head layer at d = 64 (two slices per head: 128 chains) --
+    timed with the plain scan and with the sequence split the library suggests."""
     import torch
 
     import long_context_attention_attn_amd as la
     from long_context_attention_attn_amd import _lib, synth
 
     res = []
-    for T, Hc in ((8192, 8), (65536, 8)):
-        q, k, v = synth.qkv(T, Hc, D, torch.bfloat16, seed=0, device=dev)
+    for T, Hc, Dh in ((8192, 8, D), (65536, 8, D), (65536, 64, 64)):
+        q, k, v = synth.qkv(T, Hc, Dh, torch.bfloat16, seed=0, device=dev)
         dec = synth.decay_geometric(Hc, 0.9, 0.9999).to(dev)
         o = torch.empty_like(q)
-        f = torch.empty((1, Hc, D, D), dtype=torch.float32, device=dev)
-        seg = _lib.prefill_split_blocks(T, 1, Hc, D, _lib.LA_BF16)
+        f = torch.empty((1, Hc, Dh, Dh), dtype=torch.float32, device=dev)
+        seg = _lib.prefill_split_blocks(T, 1, Hc, Dh, _lib.LA_BF16)
         plain = time_ms(lambda: la.prefill(q, k, v, dec, out=o, final_state=f), iters, warmup)
         split = time_ms(lambda: la.prefill(q, k, v, dec, out=o, final_state=f, split=seg or None),
                         iters, warmup)
-        nbytes = prefill_bytes(T, Hc, D)
-        res.append({"tokens": T, "heads": Hc, "seg_blocks": seg, "plain_ms": plain,
-                    "split_ms": split, "speedup": plain / split,
+        nbytes = prefill_bytes(T, Hc, Dh)
+        res.append({"tokens": T, "heads": Hc, "head_dim": Dh, "seg_blocks": seg,
+                    "plain_ms": plain, "split_ms": split, "speedup": plain / split,
                     "split_algorithmic_GBps": nbytes / (split / 1e3) / 1e9,
+                    "split_hbm_frac": nbytes / (split / 1e3) / 1e9 / HBM_PEAK_GBPS,
                     "split_tokens_per_s": T / (split / 1e3)})
         del q, k, v, o
     return res
