@@ -119,7 +119,8 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
  *               la_prefill and la_prefill_ex use this default
  *               64 or 128 (128: bf16 storage only, else LA_ERR_UNSUPPORTED)
  * Other arguments, result and errors as la_prefill_ex, plus LA_ERR_INVALID_ARG for any other
- * block_size.  The sequence-split prefill, the backward and the fp32 path always use B = 64.
+ * block_size.  la_backward's scans take the same default; the split prefill's segment scans
+ * pick theirs by segment length; la_backward_split and the fp32 path use B = 64.
  */
 la_status la_prefill_with_block_size(const void *q, const void *k, const void *v,
                                      const float *decay, const int32_t *cu_seqlens,
@@ -215,7 +216,8 @@ int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, 
  * Each is a scan of the same block form as the prefill: dq is the forward scan with
  * (query, key, value) = (do, v, k) from S0^T; dk and dv are reversed-time scans with (v, do, q)
  * from dSn^T and (k, q, do) from dSn; dS0 is lambda times the last of these scans' final
- * state.  Three launches on `stream`, no workspace.  lambda gets no gradient (a constant).
+ * state.  Three launches on `stream`, no workspace, with the prefill's default block size (for
+ * bf16 128 tokens, or LA_BLOCK).  lambda gets no gradient (a constant).
  *
  *   q, k, v, decay, cu_seqlens, initial_state: the forward call's inputs (initial_state may be
  *                 NULL = zeros)

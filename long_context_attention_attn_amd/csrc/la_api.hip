@@ -571,10 +571,15 @@ la_status la_backward(const void *q, const void *k, const void *v, const float *
                                 dq, dk, dv, d_initial_state, nullptr, 0, T, S, H, D, dtype);
   if (st != LA_OK) return st;
   if (T == 0 && d_initial_state == nullptr) return LA_OK;
+  // bf16: the three scans use the prefill's default block size (128, or LA_BLOCK)
+  const int block = dtype == LA_BF16 ? env_block() : 64;
+  if (block < 0) return fail(LA_ERR_INVALID_ARG, "LA_BLOCK must be 64 or 128");
   st = check_device();
   if (st != LA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto scan = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
+  auto scan = dtype == LA_F32 ? la_launch_prefill_f32
+              : block == 64   ? la_launch_prefill_bf16
+                              : la_launch_prefill_bf16_b128;
 
   LaPrefillArgs a{};
   a.decay = decay;

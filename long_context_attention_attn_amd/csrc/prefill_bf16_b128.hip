@@ -13,7 +13,10 @@
 //
 // A longer block halves the serial block steps of a chain, and with them the per-step barrier,
 // the waits for copies and the bf16 state copy, at the price of a larger intra-block product
-// (4 B d + 4 d^2 FLOP per token-head).  Forward scans only (plain and from an initial state).
+// (4 B d + 4 d^2 FLOP per token-head).  Modes as in prefill_bf16.hip, for the backward's scans:
+// a reversed scan (REV: local token t is physical token n-1-t), an initial state that counts as
+// inclusive (weight lambda^t at local token t, final state times lambda) and a transposed one;
+// and the sequence-split form (SPLIT).  No state-only form (prefill_bf16.hip has it).
 //
 // Work decomposition: as in prefill_bf16.hip, one workgroup of 8 waves per (sequence, head,
 // 32-column slice of the value dimension), workgroups mapped so that the slices of a head share an
@@ -76,18 +79,18 @@ constexpr int state_tiles() { return D / 64; }
 // L2 prefetch of the slice's share of a block's q, k and full v rows: one 16-byte read per
 // 128-byte line into a sink in LDS that nothing reads.  d = 128: four slices of 32 rows of two
 // lines; d = 64: two slices of 64 rows of one line.
-template <int D>
+template <int D, bool REV>
 __device__ __forceinline__ uint32_t prefetch_offset(int slice, int lane, uint32_t rowbytes) {
   if constexpr (D == 128)
-    return (uint32_t)(32 * slice + (lane >> 1)) * rowbytes + (uint32_t)(lane & 1) * 128u;
+    return lane_base<REV>(32 * slice + (lane >> 1), (uint32_t)(lane & 1) * 128u, rowbytes);
   else
-    return (uint32_t)(64 * slice + lane) * rowbytes;
+    return lane_base<REV>(64 * slice + lane, 0u, rowbytes);
 }
 
 // ------------------------------------------------------------------------------------------
 // Output wave W: row groups GA = W and GB = 7 - W of every block.
 // ------------------------------------------------------------------------------------------
-template <int D, int W>
+template <int D, int W, bool REV>
 __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const float *pw,
                                             int lane) {
   using C = Cfg<D>;
@@ -117,13 +120,15 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
       }
     }
   const float iscA = pw[jA + 1], iscB = pw[jB + 1];
+  // Block 0 applies the initial state; weighted lambda^j instead when it counts as inclusive.
+  const float iscA0 = c.incl ? pw[jA] : iscA, iscB0 = c.incl ? pw[jB] : iscB;
 
   // Lane offsets of the Q copies of both groups and of the stores.
   uint32_t qoffA[C::QK_DMA], qoffB[C::QK_DMA];
-  rows_offsets<D, false>(GA, lane, rowbytes, qoffA);
-  rows_offsets<D, false>(GB, lane, rowbytes, qoffB);
-  const uint32_t ooffA = (uint32_t)jA * rowbytes + 8u * g;
-  const uint32_t ooffB = (uint32_t)jB * rowbytes + 8u * g;
+  rows_offsets<D, REV>(GA, lane, rowbytes, qoffA);
+  rows_offsets<D, REV>(GB, lane, rowbytes, qoffB);
+  const uint32_t ooffA = lane_base<REV>(jA, 8u * g, rowbytes);
+  const uint32_t ooffB = lane_base<REV>(jB, 8u * g, rowbytes);
   const uint32_t qA_lds = smem_lds + C::Q_OFF + 16 * GA * C::ROWB;
   const uint32_t qB_lds = smem_lds + C::Q_OFF + 16 * GB * C::ROWB;
 
@@ -136,13 +141,13 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) vpat[ct] = (uint32_t)vswz(trow, 16 * ct + tcol);
 
-  Walk wq = walk_from<BLK, false>(c, 0), ws = walk_from<BLK, false>(c, 0);
+  Walk wq = walk_from<BLK, REV>(c, 0), ws = walk_from<BLK, REV>(c, 0);
   // Q rows of the next block into the Q buffer.
   auto issue_q = [&]() {
-    const Span sp = span_at<false>(c, wq);
-    advance<false>(c, wq);
-    dma_rows<D, false>(c.q, sp, qoffA, qA_lds);
-    dma_rows<D, false>(c.q, sp, qoffB, qB_lds);
+    const Span sp = span_at<REV>(c, wq);
+    advance<REV>(c, wq);
+    dma_rows<D, REV>(c.q, sp, qoffA, qA_lds);
+    dma_rows<D, REV>(c.q, sp, qoffB, qB_lds);
   };
   issue_q();
   wait_vm<0>();
@@ -239,10 +244,11 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
     if constexpr (NTA % 2) pA[NTA] = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 
     // O^T = lambda^(j+1) * inter + V^T P^T.
+    const float ia = i == 0 ? iscA0 : iscA, ib = i == 0 ? iscB0 : iscB;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      oA[ct] *= iscA;
-      oB[ct] *= iscB;
+      oA[ct] *= ia;
+      oB[ct] *= ib;
     }
 #pragma unroll
     for (int s = 0; s < NSB; ++s) {
@@ -259,17 +265,18 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 
     // Store: lane holds O[jX][c0 + 16 ct + 4 g + 0..3]; rows past the end are dropped.
     {
-      const Span sp = span_at<false>(c, ws);
+      const Span sp = span_at<REV>(c, ws);
       const auto ro = rsrc(c.out + sp.off, sp.bytes);
+      const uint32_t oa = at<REV>(sp, ooffA), ob = at<REV>(sp, ooffB);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(oA[ct])), ro,
-                                              ooffA + 32u * ct, 0, 0);
+                                              oa + 32u * ct, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(oB[ct])), ro,
-                                              ooffB + 32u * ct, 0, 0);
+                                              ob + 32u * ct, 0, 0);
       }
     }
-    advance<false>(c, ws);
+    advance<REV>(c, ws);
     lds_barrier();
     const uint32_t so = s_cur;
     s_cur = s_nxt;
@@ -282,7 +289,7 @@ __device__ __forceinline__ void output_wave(const Chain &c, char *smem, const fl
 // State wave R: state rows [16 RT R, 16 RT (R + 1)) of the slice.  Copies K rows
 // [BLK/4 R, BLK/4 (R + 1)); the last state wave also issues the L2 prefetches.
 // ------------------------------------------------------------------------------------------
-template <int D, int R, bool SPLIT>
+template <int D, int R, bool REV, bool SPLIT>
 __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const float *pw,
                                            const float *s0, float *fs, size_t sbase, int lane) {
   using C = Cfg<D>;
@@ -305,7 +312,8 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
         if constexpr (SPLIT)  // the incoming state of the segment, formed in the prologue
           kv[rt][ct][i] = ((const float *)(smem + SIN_OFF<D>()))[dk * CV + 16 * ct + l16];
         else
-          kv[rt][ct][i] = s0 ? s0[sbase + (size_t)dk * D + dv] : 0.f;
+          kv[rt][ct][i] =
+              s0 ? s0[sbase + (c.s0t ? (size_t)dv * D + dk : (size_t)dk * D + dv)] : 0.f;
       }
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
   uint32_t xpat[RT], kpat[RT], vpat[2];
@@ -333,49 +341,59 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
   // overwritten by the first copies of step 0).
   const int b_last = c.b_last;
   const int b0 = c.nb == 1 ? b_last : BLK;
-  const float lb_full = pw[BLK], lb_last = pw[b_last], lb_first = pw[b0];
+  // Block 0 decays the initial state by lambda^(b0 - 1) when it counts as inclusive.
+  const float lb_full = pw[BLK], lb_last = pw[b_last], lb_first = c.incl ? pw[b0 - 1] : pw[b0];
+  // Final state scale: lambda for an inclusive initial state (read now, before the stage holding
+  // the powers is overwritten).
+  const float fsc = c.incl && c.nb > 0 ? pw[1] : 1.f;
 
   // K rows [BLK/4 R, BLK/4 (R + 1)) as NG/4 16-row groups.
   constexpr int KG = NG / 4;
   uint32_t koff[KG][C::QK_DMA];
 #pragma unroll
-  for (int x = 0; x < KG; ++x) rows_offsets<D, false>(KG * R + x, lane, c.rowbytes, koff[x]);
-  const uint32_t pfoff = prefetch_offset<D>(c.slice, lane, c.rowbytes);
-  Walk wk = walk_from<BLK, false>(c, 0), wp = walk_from<BLK, false>(c, 1);
+  for (int x = 0; x < KG; ++x) rows_offsets<D, REV>(KG * R + x, lane, c.rowbytes, koff[x]);
+  const uint32_t pfoff = prefetch_offset<D, REV>(c.slice, lane, c.rowbytes);
+  Walk wk = walk_from<BLK, REV>(c, 0), wp = walk_from<BLK, REV>(c, 1);
   auto issue_k = [&](uint32_t st_off) {
-    const Span sp = span_at<false>(c, wk);
-    advance<false>(c, wk);
+    const Span sp = span_at<REV>(c, wk);
+    advance<REV>(c, wk);
 #pragma unroll
     for (int x = 0; x < KG; ++x)
-      dma_rows<D, false>(c.k, sp, koff[x], smem_lds + st_off + C::K_OFF +
+      dma_rows<D, REV>(c.k, sp, koff[x], smem_lds + st_off + C::K_OFF +
                                                16 * (KG * R + x) * C::ROWB);
   };
   // Pull the block after the next one into L2 (issued after the K copies, so that waiting for
   // them never waits for a prefetch: counters are in order).
   auto prefetch = [&]() {
     if constexpr (PF) {
-      const Span sp = span_at<false>(c, wp);
-      advance<false>(c, wp);
+      const Span sp = span_at<REV>(c, wp);
+      advance<REV>(c, wp);
       dma16_same3(rsrc(c.q + sp.off, sp.bytes), rsrc(c.k + sp.off, sp.bytes),
-                  rsrc(c.v + sp.off, sp.bytes), pfoff, smem_lds + C::PF_OFF);
+                  rsrc(c.v + sp.off, sp.bytes), at<REV>(sp, pfoff), smem_lds + C::PF_OFF);
     }
   };
   // V rows 32R..32R+31 (two 1 KiB copies) and their decayed copy lambda^(b-1-j) V[j], which the
   // state product reads.
   const int vr0 = 32 * R + lane / 4, vr1 = vr0 + 16;
-  const uint32_t voff0 = (uint32_t)vr0 * c.rowbytes + 16u * ((lane % 4) ^ vswf(vr0));
-  const uint32_t voff1 = (uint32_t)vr1 * c.rowbytes + 16u * ((lane % 4) ^ vswf(vr1)) - 1024u;
+  const uint32_t voff0 = lane_base<REV>(vr0, 16u * ((lane % 4) ^ vswf(vr0)), c.rowbytes);
+  // forward: the second copy's instruction offset adds 1 KiB back (rows >= 16)
+  const uint32_t voff1 =
+      lane_base<REV>(vr1, 16u * ((lane % 4) ^ vswf(vr1)), c.rowbytes) - (REV ? 0u : 1024u);
   const float lv0_full = pw[BLK - 1 - vr0], lv1_full = pw[BLK - 1 - vr1];
   const float lv0_last = vr0 < b_last ? pw[b_last - 1 - vr0] : 0.f;
   const float lv1_last = vr1 < b_last ? pw[b_last - 1 - vr1] : 0.f;
   const uint32_t dpat = (uint32_t)(vr0 * C::VROWB + 16 * (lane % 4));
   const char *vslice = c.v + 2 * c.c0;
-  Walk wv = walk_from<BLK, false>(c, 0);
+  Walk wv = walk_from<BLK, REV>(c, 0);
   auto issue_v = [&](uint32_t st_off) {
-    const Span sp = span_at<false>(c, wv);
-    advance<false>(c, wv);
-    dma_kib2(rsrc(vslice + sp.off, sp.bytes), voff0, voff1,
-             smem_lds + st_off + C::V_OFF + 32 * R * C::VROWB);
+    const Span sp = span_at<REV>(c, wv);
+    advance<REV>(c, wv);
+    const uint32_t lds = smem_lds + st_off + C::V_OFF + 32 * R * C::VROWB;
+    if constexpr (REV)
+      dma16x2(rsrc(vslice + sp.off, sp.bytes), at<REV>(sp, voff0), at<REV>(sp, voff1), lds,
+              lds + 1024);
+    else
+      dma_kib2(rsrc(vslice + sp.off, sp.bytes), voff0, voff1, lds);
   };
   // The decayed copy of the rows of block blk (landed in the stage at st_off), in that stage.
   auto decay_v = [&](int blk, uint32_t st_off) {
@@ -452,17 +470,17 @@ __device__ __forceinline__ void state_wave(const Chain &c, char *smem, const flo
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int dk = DK0 + 16 * rt + 4 * g + i, dv = c.c0 + 16 * ct + l16;
-          fs[sbase + (size_t)dk * D + dv] = kv[rt][ct][i];
+          fs[sbase + (size_t)dk * D + dv] = kv[rt][ct][i] * fsc;
         }
   }
 }
 
-template <int D, bool SPLIT>
+template <int D, bool REV, bool SPLIT>
 __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, __bf16 *__restrict__ out, float *__restrict__ fs, int64_t T,
-    int S, int H, int64_t seg_len, const float *__restrict__ seg_states, int nslot) {
+    int S, int H, int flags, int64_t seg_len, const float *__restrict__ seg_states, int nslot) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -500,8 +518,8 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
   c.c0 = slice * CV;
   c.slice = slice;
   c.out = (char *)(out + first + c.c0);
-  c.incl = false;
-  c.s0t = false;
+  c.incl = flags & 2;
+  c.s0t = flags & 4;
 
   const int tid = threadIdx.x;
   // Zero the stages and the Q buffer once: rows a partial block does not load then hold zeros
@@ -527,26 +545,27 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
   }
   const int lane = tid & 63;
   switch (tid >> 6) {
-    case 0: output_wave<D, 0>(c, smem, pw, lane); break;
-    case 1: output_wave<D, 1>(c, smem, pw, lane); break;
-    case 2: output_wave<D, 2>(c, smem, pw, lane); break;
-    case 3: output_wave<D, 3>(c, smem, pw, lane); break;
-    case 4: state_wave<D, 0, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 5: state_wave<D, 1, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
-    case 6: state_wave<D, 2, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
-    default: state_wave<D, 3, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 0: output_wave<D, 0, REV>(c, smem, pw, lane); break;
+    case 1: output_wave<D, 1, REV>(c, smem, pw, lane); break;
+    case 2: output_wave<D, 2, REV>(c, smem, pw, lane); break;
+    case 3: output_wave<D, 3, REV>(c, smem, pw, lane); break;
+    case 4: state_wave<D, 0, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 5: state_wave<D, 1, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    case 6: state_wave<D, 2, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
+    default: state_wave<D, 3, REV, SPLIT>(c, smem, pw, s0, fs, sbase, lane); break;
   }
 }
 
-template <int D>
+template <int D, bool REV>
 hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   const int NS = D / CV;
   const long long grid = (long long)a.S * a.H * NS;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, false>), dim3((unsigned)grid), dim3(NTHR), 0,
-                     stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+  const int flags = (a.init_inclusive ? 2 : 0) | (a.init_transposed ? 4 : 0);
+  hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, REV, false>), dim3((unsigned)grid), dim3(NTHR),
+                     0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
                      a.decay, a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state,
-                     a.T, a.S, a.H, (int64_t)0, nullptr, 0);
+                     a.T, a.S, a.H, flags, (int64_t)0, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -556,19 +575,21 @@ hipError_t launch_split(const LaPrefillArgs &a, int64_t seg_len, const float *se
   const int NS = D / CV;
   const long long grid = (long long)nslot * a.H * NS;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, true>), dim3((unsigned)grid), dim3(NTHR), 0,
-                     stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                     a.decay, a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state,
-                     a.T, a.S, a.H, seg_len, seg_states, nslot);
+  hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, false, true>), dim3((unsigned)grid),
+                     dim3(NTHR), 0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k,
+                     (const __bf16 *)a.v, a.decay, a.cu_seqlens, a.initial_state,
+                     (__bf16 *)a.out, a.final_state, a.T, a.S, a.H, 0, seg_len, seg_states,
+                     nslot);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t la_launch_prefill_bf16_b128(const LaPrefillArgs &a, hipStream_t stream) {
-  if (a.reverse || a.state_only || a.init_inclusive || a.init_transposed || a.seq_incl)
-    return hipErrorInvalidValue;  // forward scans only
-  return a.D == 128 ? launch<128>(a, stream) : launch<64>(a, stream);
+  if (a.state_only || a.seq_incl) return hipErrorInvalidValue;  // not built for this kernel
+  if (a.reverse)
+    return a.D == 128 ? launch<128, true>(a, stream) : launch<64, true>(a, stream);
+  return a.D == 128 ? launch<128, false>(a, stream) : launch<64, false>(a, stream);
 }
 
 hipError_t la_launch_prefill_split_bf16_b128(const LaPrefillArgs &a, int64_t seg_len,
