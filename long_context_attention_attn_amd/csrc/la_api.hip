@@ -668,6 +668,12 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
   const int32_t cap = (int32_t)lay.cap;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto scan = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
+  // The segment scans of long segments (>= 4,096 tokens, whole 128-token blocks) use the
+  // 128-token kernel, as the split prefill does; the state-only passes stay as they are.
+  const int64_t seg_len = (int64_t)seg_blocks * 64;
+  auto seg_scan = dtype == LA_BF16 && seg_len % 128 == 0 && seg_len >= 4096
+                      ? la_launch_prefill_bf16_b128
+                      : scan;
 
   hipError_t e = la_launch_seg_table(cu_seqlens, T, S, (int64_t)seg_blocks * 64, cap, seg_cu,
                                      seq_seg0, seg_rfirst, s);
@@ -695,7 +701,7 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
   a.initial_state = states;
   a.final_state = nullptr;
   a.state_only = false;
-  e = scan(a, s);
+  e = seg_scan(a, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "dq segments: %s", hipGetErrorString(e));
 
   // dv and dk: reversed scans (k, q, do) and (v, do, q) whose states are transposes of each
@@ -729,14 +735,14 @@ la_status la_backward_split(const void *q, const void *k, const void *v, const f
   b.state_only = false;
   b.init_inclusive = true;
   b.seq_incl = seg_rfirst;
-  e = scan(b, s);
+  e = seg_scan(b, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "dv segments: %s", hipGetErrorString(e));
   b.q = v;
   b.k = d_out;
   b.v = q;
   b.out = dk;
   b.init_transposed = true;
-  e = scan(b, s);
+  e = seg_scan(b, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, "dk segments: %s", hipGetErrorString(e));
   return LA_OK;
 }

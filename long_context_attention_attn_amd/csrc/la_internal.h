@@ -36,8 +36,8 @@ struct LaDecodeArgs {
 // Each returns the error of the launch (hipGetLastError right after it).
 hipError_t la_launch_prefill_bf16(const LaPrefillArgs &a, hipStream_t stream);
 hipError_t la_launch_prefill_f32(const LaPrefillArgs &a, hipStream_t stream);
-// bf16 prefill with 128-token blocks (prefill_bf16_b128.hip): every mode but state_only and
-// seq_incl (hipErrorInvalidValue for those).
+// bf16 prefill with 128-token blocks (prefill_bf16_b128.hip): every mode but state_only
+// (hipErrorInvalidValue).
 hipError_t la_launch_prefill_bf16_b128(const LaPrefillArgs &a, hipStream_t stream);
 hipError_t la_launch_decode_bf16(const LaDecodeArgs &a, hipStream_t stream);
 hipError_t la_launch_decode_f32(const LaDecodeArgs &a, hipStream_t stream);

@@ -15,8 +15,9 @@
 // the waits for copies and the bf16 state copy, at the price of a larger intra-block product
 // (4 B d + 4 d^2 FLOP per token-head).  Modes as in prefill_bf16.hip, for the backward's scans:
 // a reversed scan (REV: local token t is physical token n-1-t), an initial state that counts as
-// inclusive (weight lambda^t at local token t, final state times lambda) and a transposed one;
-// and the sequence-split form (SPLIT).  No state-only form (prefill_bf16.hip has it).
+// inclusive (weight lambda^t at local token t, final state times lambda; optionally only for
+// flagged sequences) and a transposed one; and the sequence-split form (SPLIT).  No state-only
+// form (prefill_bf16.hip has it).
 //
 // Work decomposition: as in prefill_bf16.hip, one workgroup of 8 waves per (sequence, head,
 // 32-column slice of the value dimension), workgroups mapped so that the slices of a head share an
@@ -480,7 +481,8 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, __bf16 *__restrict__ out, float *__restrict__ fs, int64_t T,
-    int S, int H, int flags, int64_t seg_len, const float *__restrict__ seg_states, int nslot) {
+    int S, int H, int flags, const int32_t *__restrict__ incl_v, int64_t seg_len,
+    const float *__restrict__ seg_states, int nslot) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -518,7 +520,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
   c.c0 = slice * CV;
   c.slice = slice;
   c.out = (char *)(out + first + c.c0);
-  c.incl = flags & 2;
+  // flags bit 1: inclusive initial state (only for sequences s with incl_v[s] != 0 when incl_v
+  // is given); bit 2: transposed initial state
+  c.incl = (flags & 2) && (incl_v == nullptr || incl_v[seq] != 0);
   c.s0t = flags & 4;
 
   const int tid = threadIdx.x;
@@ -565,7 +569,7 @@ hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, REV, false>), dim3((unsigned)grid), dim3(NTHR),
                      0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
                      a.decay, a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state,
-                     a.T, a.S, a.H, flags, (int64_t)0, nullptr, 0);
+                     a.T, a.S, a.H, flags, a.seq_incl, (int64_t)0, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -578,15 +582,15 @@ hipError_t launch_split(const LaPrefillArgs &a, int64_t seg_len, const float *se
   hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, false, true>), dim3((unsigned)grid),
                      dim3(NTHR), 0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k,
                      (const __bf16 *)a.v, a.decay, a.cu_seqlens, a.initial_state,
-                     (__bf16 *)a.out, a.final_state, a.T, a.S, a.H, 0, seg_len, seg_states,
-                     nslot);
+                     (__bf16 *)a.out, a.final_state, a.T, a.S, a.H, 0, nullptr, seg_len,
+                     seg_states, nslot);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t la_launch_prefill_bf16_b128(const LaPrefillArgs &a, hipStream_t stream) {
-  if (a.state_only || a.seq_incl) return hipErrorInvalidValue;  // not built for this kernel
+  if (a.state_only) return hipErrorInvalidValue;  // not built for this kernel
   if (a.reverse)
     return a.D == 128 ? launch<128, true>(a, stream) : launch<64, true>(a, stream);
   return a.D == 128 ? launch<128, false>(a, stream) : launch<64, false>(a, stream);

@@ -192,9 +192,10 @@ def test_split_two_launch_path_packed(D):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("seg_blocks", [64, 66])
 def test_split_long_segment_kernels(D, seg_blocks):
-    """Segments of 4,096 tokens (whole 128-token blocks: the 128-token segment prefill) and of
-    4,224 tokens (the 64-token one) over packed sequences with an empty one and a partial last
-    block, from initial states, against the recurrent form."""
+    """Segments of 4,096 tokens (whole 128-token blocks: the 128-token segment scans) and of
+    4,224 tokens (the 64-token ones) over packed sequences with an empty one and a partial last
+    block, from initial states: the split prefill against the recurrent form, the split
+    backward against O7."""
     lengths = [9000, 0, 4096, 5000, 129]
     H = 2
     banner("split long segment kernels D=%d seg_blocks=%d" % (D, seg_blocks))
@@ -212,3 +213,15 @@ def test_split_long_segment_kernels(D, seg_blocks):
     print("long segments D=%d seg=%d: out %.2e state %.2e" % (D, seg_blocks, e, es))
     assert e <= BF16_TOL and es <= BF16_TOL
     assert torch.equal(fs.cpu()[1], init[1])
+    # the split backward over the same segments (its reversed segment scans with per-sequence
+    # inclusive states) against O7
+    do, _, _ = synth.qkv(int(cu[-1]), H, D, torch.bfloat16, seed=65)
+    dfs = synth.random_state(len(lengths), H, D, seed=66, scale=0.1)
+    g = la.backward(q.to(d), k.to(d), v.to(d), decay.to(d), do.to(d), cu.to(d),
+                    initial_state=init.to(d), d_final_state=dfs.to(d), split=seg_blocks)
+    torch.cuda.synchronize()
+    want = oracle.backward_recurrent(q, k, v, decay, do, cu, init_state=init, d_final=dfs)
+    eg = [float(slice_errors(to_np(x), w, cu).max()) for x, w in zip(g[:3], want[:3])]
+    eg.append(float(state_errors(to_np(g[3]), want[3]).max()))
+    print("  backward: dq %.2e dk %.2e dv %.2e d_init %.2e" % tuple(eg))
+    assert max(eg) <= BF16_TOL
