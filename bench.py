@@ -38,7 +38,7 @@ T_PREFILL, H, D = 65536, 64, 128
 BT_DECODE = 256
 BLOCK_FLOP_B = 64              # FLOP accounting at block size 64, whatever the kernel's B
 KERNEL_BLOCK = 128             # the bf16 prefill's block size (the library default)
-PREFILL_KERNEL = "prefill_bf16_b128_kernel<128>"
+PREFILL_KERNEL = "prefill_bf16_b128_kernel<128, false, false>"
 # sources the committed profiles of that kernel were taken with
 PREFILL_SOURCES = ("long_context_attention_attn_amd/csrc/prefill_bf16_b128.hip",
                    "long_context_attention_attn_amd/csrc/bf16_tiles.h")
