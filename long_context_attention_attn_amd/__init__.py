@@ -66,7 +66,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
     sequence split with the segment length the library suggests for this device, or the plain
     scan when it suggests none.  All give the same result up to rounding order.
     block_size: 0 = the library's default, or 64 / 128 tokens per block (128: bf16 only; the
-    sequence split always uses 64).  Every block size gives the same result up to rounding.
+    sequence split ignores it and picks the block size by segment length).  Every block size
+    gives the same result up to rounding.
     static_scratch: with a sequence split, keep its segment states in the library's static
     device scratch (la_prefill_split_static) instead of a torch-allocated workspace, so the
     library call allocates nothing; needs la_prefill_split_workspace_size <= 32 MiB.  Calls

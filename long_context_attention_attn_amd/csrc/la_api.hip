@@ -490,9 +490,16 @@ int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, 
   double w_split = (double)((blocks + seg - 1) / seg + S - 1) * H * slices;  // all segments
   if (w_split > compute_units) w_split = compute_units;
   const double plain = 6.0 + (double)nb * block_cost(dtype, D, w_plain, bytes);
-  const double so = dtype == LA_F32 ? 0.75 : 0.55;
+  double so = dtype == LA_F32 ? 0.75 : 0.55;
+  const int64_t count = (nb + seg - 1) / seg;  // segments of a (mean) sequence
+  // The two-launch bf16 form computes no state for the last segment of a sequence; its state
+  // pass then runs fewer workgroups (measured: two segments per sequence save about a quarter
+  // of the pass, eight about 6%).
+  if (dtype == LA_BF16 && (blocks + seg - 1) / seg <= kFusedMaxSegments &&
+      ((int64_t)seg * 64 + 64) * (int64_t)H * D * 2 < (int64_t(1) << 31))
+    so *= ((double)count - 0.5) / (double)count;
   const double split = 17.0 + (double)seg * block_cost(dtype, D, w_split, bytes) * (1.0 + so) +
-                       0.5 * (double)((nb + seg - 1) / seg);
+                       0.5 * (double)count;
   if (split >= 0.95 * plain) return 0;
   return (int32_t)seg;
 }

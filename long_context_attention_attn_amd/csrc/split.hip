@@ -193,7 +193,9 @@ __device__ __forceinline__ bf16x4 tr_read4(const char *p) {
 // The segment table is either read (cu = segment starts, FUSED = false) or found by the
 // workgroup itself (FUSED: cu = the sequences' cu_seqlens, slot = segment as in seg_lookup.h);
 // the fused form also writes the final states of empty sequences (their initial states, or
-// zeros), the one thing the segment prefill that follows cannot do.
+// zeros), the one thing the segment prefill that follows cannot do, and computes no state for
+// the last segment of a sequence (nothing reads it: that segment's prefill writes the sequence's
+// final state).
 struct FusedSeg {
   int64_t T;
   int S;
@@ -230,10 +232,14 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
   }
   const int seg = chain / H, h = chain % H;
   int64_t tok0, tok1;
+  bool skip = false;  // FUSED: no state to compute for this slot
   if constexpr (FUSED) {
     const SegPos sp = find_segment(cu, fz.T, fz.S, fz.seg_len, seg);
     tok0 = sp.seq >= 0 ? sp.tok0 : 0;
     tok1 = sp.seq >= 0 ? sp.tok1 : 0;
+    // Only the segments before the last of each sequence feed a later segment's incoming state;
+    // the last one's prefill writes the sequence's final state itself.  Unused slots have none.
+    skip = sp.seq < 0 || sp.j == sp.count - 1;
   } else {
     tok0 = cu[seg];
     tok1 = cu[seg + 1];
@@ -254,6 +260,7 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
         }
       }
     }
+    if (skip) return;  // the whole workgroup (the segment lookup is wave-uniform)
   }
   const double lam = (double)decay[h];
 

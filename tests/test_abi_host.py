@@ -336,10 +336,12 @@ SPLIT_MEASURED = [
 # Several sequences (S equal lengths of T / S tokens), timed the same way: (dtype, D, H, S, T,
 # split wins).  fp32 D = 64 one head, 8 x 1,024 tokens: plain 47.0 us / split 35.5; fp32
 # D = 128 74.3 / 48.7; bf16 D = 128 17.9 / 25.1; bf16 D = 64 13.8 / 22.4; bf16 D = 64
-# H = 4, 4 x 8,192: 76.6 / 41.1; fp32 D = 128 H = 8, 2 x 32,768: 2234 / 971.
+# H = 4, 4 x 8,192: 76.6 / 41.1; fp32 D = 128 H = 8, 2 x 32,768: 2234 / 971; bf16 D = 128
+# H = 16, 2 x 8,192 (two segments per sequence, the last one's state not computed): 103.3 / 91.4.
 SPLIT_MEASURED_BATCHED = [
     (0, 64, 1, 8, 8192, True), (0, 128, 1, 8, 8192, True), (1, 128, 1, 8, 8192, False),
     (1, 64, 1, 8, 8192, False), (1, 64, 4, 4, 32768, True), (0, 128, 8, 2, 65536, True),
+    (1, 128, 16, 2, 16384, True),
 ]
 
 
