@@ -119,8 +119,9 @@ la_status la_prefill_ex(const void *q, const void *k, const void *v, const float
  *               la_prefill and la_prefill_ex use this default
  *               64 or 128 (128: bf16 storage only, else LA_ERR_UNSUPPORTED)
  * Other arguments, result and errors as la_prefill_ex, plus LA_ERR_INVALID_ARG for any other
- * block_size.  la_backward's scans take the same default; the split prefill's segment scans
- * pick theirs by segment length; la_backward_split and the fp32 path use B = 64.
+ * block_size.  la_backward's scans take the same default; the segment scans of the split
+ * prefill and of la_backward_split pick theirs by segment length (128 for segments of 4,096
+ * tokens or more in whole 128-token blocks); the fp32 path uses B = 64.
  */
 la_status la_prefill_with_block_size(const void *q, const void *k, const void *v,
                                      const float *decay, const int32_t *cu_seqlens,
@@ -136,12 +137,16 @@ la_status la_prefill_with_block_size(const void *q, const void *k, const void *v
  *
  * The block recurrence (digest, section 1: the running state of the right product) is linear
  * in the state, so a segment of m tokens maps its incoming state S_in to lambda^m S_in + L with
- * L independent of S_in.  Four launches on `stream`: a segment table built from cu_seqlens on
- * the device; L of every segment (k and v read once); a combine that walks each sequence's
- * segments in order (incoming state of the first = initial_state or 0, final state = what
- * follows the last); the prefill of every segment from its incoming state.  q, k and v are read
- * twice in total (k and v in both scans), out is written once.  The result differs from
- * la_prefill_ex only in rounding order.
+ * L independent of S_in.  bf16 storage (while no sequence has more than 16 segments and a
+ * segment's byte offsets fit 32 bits): two launches on `stream`, L of every segment but the
+ * last of each sequence (k and v read once; computed as 2, 4 or 8 sub-segment states when
+ * those segments are too few to fill the device), then the prefill of every segment, which
+ * forms its incoming state from the earlier segments' states (the first from initial_state or
+ * 0) and, for the last segment, writes the final state.  Otherwise four launches: a segment
+ * table built from cu_seqlens on the device; L of every segment; a combine that walks each
+ * sequence's segments in order (final state = what follows the last); the prefill of every
+ * segment from its incoming state.  k and v are read twice in total, q once, out is written
+ * once.  The result differs from la_prefill_ex only in rounding order.
  *
  *   seg_blocks       >= 1: segment length in 64-token blocks (la_prefill_split_blocks suggests
  *                    one for the current device)
@@ -182,8 +187,10 @@ la_status la_prefill_split_static(const void *q, const void *k, const void *v,
                                   int32_t seg_blocks, void *stream);
 
 /* Workspace bytes la_prefill_split and la_backward_split need for these sizes (0 for invalid
- * sizes).  The bound holds for any valid cu_seqlens: (ceil(T / (64 seg_blocks)) + S - 1) states
- * of H*D*D floats plus the segment table. */
+ * sizes).  The bound holds for any valid cu_seqlens: (ceil(T / (64 seg_blocks)) + S - 1) * sub
+ * states of H*D*D floats plus the segment table, where sub (1, 2, 4 or 8; a function of these
+ * sizes only) is the number of sub-segment states per segment that the bf16 two-launch form may
+ * keep. */
 size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t D,
                                        int32_t seg_blocks);
 

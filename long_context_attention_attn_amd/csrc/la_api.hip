@@ -114,9 +114,6 @@ int env_block() {
 constexpr int kMaxDevices = 64;
 // Size of the static scratch of la_prefill_split_static (per device).
 constexpr size_t kScratchBytes = LA_SPLIT_STATIC_SCRATCH_BYTES;
-// Most segments per sequence for which the bf16 split forms incoming states in the segment
-// prefill's prologue instead of a separate combine launch.
-constexpr int64_t kFusedMaxSegments = 16;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];   // 1 = gfx950, 0 = other arch
 int g_dev_cus[kMaxDevices];  // compute units
@@ -169,14 +166,48 @@ int64_t split_capacity(int64_t T, int32_t S, int64_t seg_len) {
 
 struct SplitLayout {
   int64_t cap;
+  int32_t sub;  // state slots per segment slot
   size_t states, seg_cu, seq_seg0, seg_rfirst, bytes;  // byte offsets and total size
 };
 
-SplitLayout split_layout(int64_t T, int32_t S, int32_t H, int32_t D, int32_t seg_blocks) {
+// Most segments per sequence for which the bf16 split forms incoming states in the segment
+// prefill's prologue instead of a separate combine launch.
+constexpr int64_t kFusedMaxSegments = 16;
+
+// Whether the bf16 split runs as two launches (segment states found on the device, incoming
+// states formed in the segment prefill's prologue): while each segment's 32-bit byte offsets
+// hold and no sequence can have more than kFusedMaxSegments segments.
+bool split_fused(int64_t T, int32_t H, int32_t D, int64_t seg_len) {
+  return (seg_len + 64) * (int64_t)H * D * 2 < (int64_t(1) << 31) &&
+         (T + seg_len - 1) / seg_len <= kFusedMaxSegments;
+}
+
+// Sub-segments per segment of the two-launch form's state pass.  Only the segments before the
+// last of each sequence need a state; when they are too few to fill the device (one
+// sequence cut in two: a workgroup per head and 32 columns), their states are computed in
+// sub-segments of seg_len / sub tokens by sub times as many, shorter workgroups (the segment
+// prefill adds sub states per earlier segment).  Doubled while the state pass stays within one
+// round of workgroups on 256 compute units (one workgroup per CU at d = 128, two at d = 64: its
+// LDS), sub-segments keep at least 2,048 tokens, and a segment's prologue adds at most 16
+// states.  A function of the sizes only, so the workspace size needs no device.
+int32_t split_sub(int64_t T, int32_t S, int32_t H, int32_t D, int64_t seg_len) {
+  const int64_t segs = (T + seg_len - 1) / seg_len;  // segments of all sequences (at most)
+  const int64_t need = segs > S ? segs - S : 1;       // segments before a sequence's last
+  const int64_t wgs = need * H * (D / 32), round = D == 64 ? 512 : 256;
+  int32_t sub = 1;
+  while (sub < 8 && wgs * sub * 2 <= round && seg_len % (sub * 2) == 0 &&
+         seg_len / (sub * 2) >= 2048 && (segs - 1) * sub * 2 <= 16)
+    sub *= 2;
+  return sub;
+}
+
+SplitLayout split_layout(int64_t T, int32_t S, int32_t H, int32_t D, int32_t seg_blocks,
+                         int32_t sub = 1) {
   SplitLayout l;
   l.cap = split_capacity(T, S, (int64_t)seg_blocks * 64);
+  l.sub = sub;
   l.states = 0;
-  l.seg_cu = align256((size_t)l.cap * H * D * D * sizeof(float));
+  l.seg_cu = align256((size_t)l.cap * sub * H * D * D * sizeof(float));
   l.seq_seg0 = l.seg_cu + align256((size_t)(l.cap + 1) * sizeof(int32_t));
   l.seg_rfirst = l.seq_seg0 + align256((size_t)(S + 1) * sizeof(int32_t));
   l.bytes = l.seg_rfirst + align256((size_t)l.cap * sizeof(int32_t));
@@ -266,8 +297,14 @@ la_status prefill_split_impl(const void *q, const void *k, const void *v, const 
   if (T == 0)  // no segments: final states are the initial states (or zeros)
     return la_prefill_ex(q, k, v, decay, cu_seqlens, initial_state, out, final_state, T, S, H,
                          D, dtype, stream);
-  const SplitLayout lay = split_layout(T, S, H, D, seg_blocks);
-  if (lay.cap * H * (D / 32) > 0x7fffffffLL || (long long)S * H * (D * D / 256) > 0x7fffffffLL)
+  const int64_t seg_len = (int64_t)seg_blocks * 64;
+  const bool fused = dtype == LA_BF16 && split_fused(T, H, D, seg_len);
+  SplitLayout lay =
+      split_layout(T, S, H, D, seg_blocks, fused ? split_sub(T, S, H, D, seg_len) : 1);
+  // the static scratch takes the sub-segment states only when they fit
+  if (static_scratch && lay.bytes > kScratchBytes) lay = split_layout(T, S, H, D, seg_blocks, 1);
+  if (lay.cap * lay.sub * H * (D / 32) > 0x7fffffffLL ||
+      (long long)S * H * (D * D / 256) > 0x7fffffffLL)
     return fail(LA_ERR_INVALID_ARG, "too many segments");
   if (static_scratch) {
     if (lay.bytes > kScratchBytes)
@@ -300,17 +337,14 @@ la_status prefill_split_impl(const void *q, const void *k, const void *v, const 
   const int32_t cap = (int32_t)lay.cap;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto prefill = dtype == LA_BF16 ? la_launch_prefill_bf16 : la_launch_prefill_f32;
-  const int64_t seg_len = (int64_t)seg_blocks * 64;
 
   // bf16, two launches: the segment states (each workgroup finds its segment in cu_seqlens),
   // then every segment from the incoming state its workgroup forms from the earlier segments'
-  // states (no table, no combine launch).  Used while each segment's 32-bit byte offsets hold
-  // and no sequence has more than kFusedMaxSegments segments (a segment's prologue reads every
-  // earlier segment's state of its sequence).
-  if (dtype == LA_BF16 && (seg_len + 64) * (int64_t)H * D * 2 < (int64_t(1) << 31) &&
-      (T + seg_len - 1) / seg_len <= kFusedMaxSegments) {
-    hipError_t e = la_launch_segment_states_fused_bf16(cu_seqlens, T, S, seg_len, cap, k, v,
-                                                       decay, H, D, states, initial_state,
+  // states (no table, no combine launch; a segment's prologue reads every earlier segment's
+  // states of its sequence).
+  if (fused) {
+    hipError_t e = la_launch_segment_states_fused_bf16(cu_seqlens, T, S, seg_len, lay.sub, cap,
+                                                       k, v, decay, H, D, states, initial_state,
                                                        final_state, s);
     if (e != hipSuccess) return fail(LA_ERR_HIP, "segment state launch: %s", hipGetErrorString(e));
     LaPrefillArgs a{};
@@ -329,8 +363,8 @@ la_status prefill_split_impl(const void *q, const void *k, const void *v, const 
     // Long segments run the 128-token kernel (measured: 8,192-token segments 2.6% faster);
     // short ones the 64-token kernel (1,024-token segments: 5% faster than 128).
     e = seg_len % 128 == 0 && seg_len >= 4096
-            ? la_launch_prefill_split_bf16_b128(a, seg_len, states, cap, s)
-            : la_launch_prefill_split_bf16(a, seg_len, states, cap, s);
+            ? la_launch_prefill_split_bf16_b128(a, seg_len, states, cap, lay.sub, s)
+            : la_launch_prefill_split_bf16(a, seg_len, states, cap, lay.sub, s);
     if (e != hipSuccess)
       return fail(LA_ERR_HIP, "segment prefill launch: %s", hipGetErrorString(e));
     return LA_OK;
@@ -464,7 +498,10 @@ la_status la_prefill(const void *q, const void *k, const void *v, const float *d
 size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t D,
                                        int32_t seg_blocks) {
   if (T < 0 || S < 1 || H < 1 || (D != 64 && D != 128) || seg_blocks < 1) return 0;
-  return split_layout(T, S, H, D, seg_blocks).bytes;
+  const int64_t seg_len = (int64_t)seg_blocks * 64;
+  // the larger of the two forms: the bf16 two-launch one may keep sub-segment states
+  const int32_t sub = T > 0 && split_fused(T, H, D, seg_len) ? split_sub(T, S, H, D, seg_len) : 1;
+  return split_layout(T, S, H, D, seg_blocks, sub).bytes;
 }
 
 int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype,
@@ -495,8 +532,7 @@ int32_t la_prefill_split_blocks_for(int64_t T, int32_t S, int32_t H, int32_t D, 
   // The two-launch bf16 form computes no state for the last segment of a sequence; its state
   // pass then runs fewer workgroups (measured: two segments per sequence save about a quarter
   // of the pass, eight about 6%).
-  if (dtype == LA_BF16 && (blocks + seg - 1) / seg <= kFusedMaxSegments &&
-      ((int64_t)seg * 64 + 64) * (int64_t)H * D * 2 < (int64_t(1) << 31))
+  if (dtype == LA_BF16 && split_fused(T, H, D, seg * 64))
     so *= ((double)count - 0.5) / (double)count;
   const double split = 17.0 + (double)seg * block_cost(dtype, D, w_split, bytes) * (1.0 + so) +
                        0.5 * (double)count;

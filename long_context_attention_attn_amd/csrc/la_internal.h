@@ -59,21 +59,23 @@ hipError_t la_launch_segment_states_bf16(const LaPrefillArgs &a, int64_t max_len
 // The split prefill in two launches (bf16 storage, forward): the segment-state pass finds each
 // workgroup's segment from the sequences' cu_seqlens itself (no table) and writes the final
 // states of empty sequences; the segment prefill finds its segment the same way and forms its
-// incoming state from the earlier segments' states in its prologue (no combine pass).  Slots
-// 0 .. cap-1 as in la_launch_seg_table; a.cu_seqlens, a.S: the sequences; a.initial_state,
+// incoming state from the earlier segments' states in its prologue (no combine pass).  Segment
+// slots 0 .. cap-1 as in la_launch_seg_table; the state pass cuts each into `sub` sub-segments
+// of seg_len / sub tokens (states slot g * sub + i, cap * sub slots) and computes none for the
+// last segment of a sequence.  a.cu_seqlens, a.S: the sequences; a.initial_state,
 // a.final_state: the sequences' states.
 hipError_t la_launch_segment_states_fused_bf16(const int32_t *cu_seqlens, int64_t T, int32_t S,
-                                               int64_t seg_len, int32_t cap, const void *k,
-                                               const void *v, const float *decay, int32_t H,
-                                               int32_t D, float *states, const float *s0,
-                                               float *fs, hipStream_t stream);
+                                               int64_t seg_len, int32_t sub, int32_t cap,
+                                               const void *k, const void *v, const float *decay,
+                                               int32_t H, int32_t D, float *states,
+                                               const float *s0, float *fs, hipStream_t stream);
 hipError_t la_launch_prefill_split_bf16(const LaPrefillArgs &a, int64_t seg_len,
-                                        const float *seg_states, int32_t nslot,
+                                        const float *seg_states, int32_t nslot, int32_t sub,
                                         hipStream_t stream);
 // The same with 128-token blocks (seg_len a multiple of 128).
 hipError_t la_launch_prefill_split_bf16_b128(const LaPrefillArgs &a, int64_t seg_len,
                                              const float *seg_states, int32_t nslot,
-                                             hipStream_t stream);
+                                             int32_t sub, hipStream_t stream);
 // s0_transposed: read s0[s][h][b][a] as element [a][b].  reverse_inclusive: walk each sequence's
 // segments from last to first (a reversed scan), the first one counting s0 as inclusive.
 hipError_t la_launch_combine(const float *decay, const int32_t *seg_cu, const int32_t *seq_seg0,

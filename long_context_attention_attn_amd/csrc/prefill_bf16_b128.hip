@@ -482,7 +482,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
     const float *__restrict__ decay, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, __bf16 *__restrict__ out, float *__restrict__ fs, int64_t T,
     int S, int H, int flags, const int32_t *__restrict__ incl_v, int64_t seg_len,
-    const float *__restrict__ seg_states, int nslot) {
+    const float *__restrict__ seg_states, int nslot, int sub) {
   using C = Cfg<D>;
   constexpr int NS = D / CV;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -540,8 +540,8 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_b128_kernel(
   __syncthreads();  // pw and zeroed buffers visible before any copy or read
   size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   if constexpr (SPLIT) {
-    split_incoming_state<D, CV, NTHR>((float *)(smem + SIN_OFF<D>()), s0, seg_states, sp, H, h,
-                                      c.c0, seg_decay(decay[h], seg_len), tid);
+    split_incoming_state<D, CV, NTHR>((float *)(smem + SIN_OFF<D>()), s0, seg_states, sp, sub,
+                                      H, h, c.c0, seg_decay(decay[h], seg_len / sub), tid);
     __syncthreads();
     // the final state is the sequence's, written by its last segment only
     sbase = ((size_t)sp.seq * H + h) * (size_t)D * D;
@@ -569,13 +569,13 @@ hipError_t launch(const LaPrefillArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_bf16_b128_kernel<D, REV, false>), dim3((unsigned)grid), dim3(NTHR),
                      0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
                      a.decay, a.cu_seqlens, a.initial_state, (__bf16 *)a.out, a.final_state,
-                     a.T, a.S, a.H, flags, a.seq_incl, (int64_t)0, nullptr, 0);
+                     a.T, a.S, a.H, flags, a.seq_incl, (int64_t)0, nullptr, 0, 1);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_split(const LaPrefillArgs &a, int64_t seg_len, const float *seg_states,
-                        int32_t nslot, hipStream_t stream) {
+                        int32_t nslot, int32_t sub, hipStream_t stream) {
   const int NS = D / CV;
   const long long grid = (long long)nslot * a.H * NS;
   if (grid <= 0) return hipSuccess;
@@ -583,7 +583,7 @@ hipError_t launch_split(const LaPrefillArgs &a, int64_t seg_len, const float *se
                      dim3(NTHR), 0, stream, (const __bf16 *)a.q, (const __bf16 *)a.k,
                      (const __bf16 *)a.v, a.decay, a.cu_seqlens, a.initial_state,
                      (__bf16 *)a.out, a.final_state, a.T, a.S, a.H, 0, nullptr, seg_len,
-                     seg_states, nslot);
+                     seg_states, nslot, sub);
   return hipGetLastError();
 }
 
@@ -598,8 +598,9 @@ hipError_t la_launch_prefill_bf16_b128(const LaPrefillArgs &a, hipStream_t strea
 
 hipError_t la_launch_prefill_split_bf16_b128(const LaPrefillArgs &a, int64_t seg_len,
                                              const float *seg_states, int32_t nslot,
-                                             hipStream_t stream) {
+                                             int32_t sub, hipStream_t stream) {
   if (seg_len % BLK != 0) return hipErrorInvalidValue;  // segments of whole 128-token blocks
-  return a.D == 128 ? launch_split<128>(a, seg_len, seg_states, nslot, stream)
-                    : launch_split<64>(a, seg_len, seg_states, nslot, stream);
+  if (sub < 1 || seg_len % sub != 0) return hipErrorInvalidValue;
+  return a.D == 128 ? launch_split<128>(a, seg_len, seg_states, nslot, sub, stream)
+                    : launch_split<64>(a, seg_len, seg_states, nslot, sub, stream);
 }

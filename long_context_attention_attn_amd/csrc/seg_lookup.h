@@ -86,14 +86,19 @@ __device__ __forceinline__ float seg_decay(float lam, int64_t m) {
 
 // The incoming state S_in of a segment's CV-column value slice, formed by the workgroup that
 // prefills the segment (NTHR threads, D * CV / NTHR consecutive elements each) from the states
-// an earlier pass left for the earlier segments of its sequence:
-//   S_in(0) = the sequence's initial state (or zero),  S_in(j) = lambda^L S_in(j-1) + L(j-1),
-// in fp32 with one fmaf per step (the rounding of a separate combine pass over the same states).
-// s0: [S][H][D][D] or nullptr; states: [slots][H][D][D]; sin: the [D][CV] fp32 result (LDS).
+// an earlier pass left for the earlier segments of its sequence.  That pass may cut every
+// segment into `sub` sub-segments of L / sub tokens (slot g * sub + i is sub-segment i of
+// segment slot g; the earlier segments of a sequence are whole, so all their sub-segments are
+// full): with x = 0 .. j * sub - 1 running over the sub-segments before segment j,
+//   S_in = the sequence's initial state (or zero),  S_in = lambda^(L/sub) S_in + L(x),
+// in fp32 with one fmaf per step (for sub = 1 the rounding of a separate combine pass).
+// s0: [S][H][D][D] or nullptr; states: [slots * sub][H][D][D]; sin: the [D][CV] fp32 result
+// (LDS); lam_l = lambda^(L/sub).
 template <int D, int CV, int NTHR>
 __device__ __forceinline__ void split_incoming_state(float *sin, const float *s0,
                                                      const float *states, const SegPos &sp,
-                                                     int H, int h, int c0, float lam_l, int tid) {
+                                                     int sub, int H, int h, int c0, float lam_l,
+                                                     int tid) {
   typedef __attribute__((ext_vector_type(4))) float f4;
   constexpr int E = D * CV / NTHR;  // elements per thread, consecutive columns
   static_assert(E % 4 == 0 && CV % E == 0, "whole 16-byte pieces of one row per thread");
@@ -104,19 +109,21 @@ __device__ __forceinline__ void split_incoming_state(float *sin, const float *s0
   const float *src0 = s0 ? s0 + ((size_t)sp.seq * H + h) * DD + off : nullptr;
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = src0 ? src0[e] : 0.f;
-  constexpr int NB = 8;  // earlier segments loaded per batch, all loads in flight together
-  for (int jb = 0; jb < sp.j; jb += NB) {
+  constexpr int NB = 8;  // earlier states loaded per batch, all loads in flight together
+  const int nx = sp.j * sub;                 // sub-segment states before segment j
+  const size_t x0 = (size_t)sp.first * sub;  // slot of the sequence's first one
+  for (int jb = 0; jb < nx; jb += NB) {
     f4 buf[NB][E / 4];
 #pragma unroll
     for (int x = 0; x < NB; ++x)
-      if (jb + x < sp.j) {
-        const float *p = states + ((size_t)(sp.first + jb + x) * H + h) * DD + off;
+      if (jb + x < nx) {
+        const float *p = states + ((x0 + jb + x) * H + h) * DD + off;
 #pragma unroll
         for (int u = 0; u < E / 4; ++u) buf[x][u] = *(const f4 *)(p + 4 * u);
       }
 #pragma unroll
     for (int x = 0; x < NB; ++x)
-      if (jb + x < sp.j) {
+      if (jb + x < nx) {
 #pragma unroll
         for (int u = 0; u < E / 4; ++u)
 #pragma unroll

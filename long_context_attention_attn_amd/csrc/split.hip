@@ -200,6 +200,8 @@ struct FusedSeg {
   int64_t T;
   int S;
   int64_t seg_len;
+  int sub;          // sub-segments per segment: workgroup slot g * sub + i covers tokens
+                    // [i, i + 1) * seg_len / sub of segment slot g
   const float *s0;  // [S][H][D][D] initial states or nullptr
   float *fs_seq;    // [S][H][D][D] final states or nullptr
 };
@@ -234,11 +236,13 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
   int64_t tok0, tok1;
   bool skip = false;  // FUSED: no state to compute for this slot
   if constexpr (FUSED) {
-    const SegPos sp = find_segment(cu, fz.T, fz.S, fz.seg_len, seg);
-    tok0 = sp.seq >= 0 ? sp.tok0 : 0;
-    tok1 = sp.seq >= 0 ? sp.tok1 : 0;
-    // Only the segments before the last of each sequence feed a later segment's incoming state;
-    // the last one's prefill writes the sequence's final state itself.  Unused slots have none.
+    const SegPos sp = find_segment(cu, fz.T, fz.S, fz.seg_len, seg / fz.sub);
+    const int64_t ls = fz.seg_len / fz.sub;  // tokens of a sub-segment
+    tok0 = sp.seq >= 0 ? sp.tok0 + (int64_t)(seg % fz.sub) * ls : 0;
+    tok1 = sp.seq >= 0 ? (tok0 + ls < sp.tok1 ? tok0 + ls : sp.tok1) : 0;
+    // Only the segments before the last of each sequence feed a later segment's incoming state
+    // (and they are whole, so each of their sub-segments is full); the last one's prefill writes
+    // the sequence's final state itself.  Unused slots have none.
     skip = sp.seq < 0 || sp.j == sp.count - 1;
   } else {
     tok0 = cu[seg];
@@ -451,13 +455,14 @@ hipError_t la_launch_segment_states_bf16(const LaPrefillArgs &a, int64_t max_len
 }
 
 hipError_t la_launch_segment_states_fused_bf16(const int32_t *cu_seqlens, int64_t T, int32_t S,
-                                               int64_t seg_len, int32_t cap, const void *k,
-                                               const void *v, const float *decay, int32_t H,
-                                               int32_t D, float *states, const float *s0,
-                                               float *fs, hipStream_t stream) {
-  const long long grid = (long long)cap * H * (D / SS_CV);
+                                               int64_t seg_len, int32_t sub, int32_t cap,
+                                               const void *k, const void *v, const float *decay,
+                                               int32_t H, int32_t D, float *states,
+                                               const float *s0, float *fs, hipStream_t stream) {
+  if (sub < 1 || seg_len % sub != 0) return hipErrorInvalidValue;
+  const long long grid = (long long)cap * sub * H * (D / SS_CV);
   if (grid <= 0) return hipSuccess;
-  const FusedSeg fz{T, S, seg_len, s0, fs};
+  const FusedSeg fz{T, S, seg_len, sub, s0, fs};
   if (D == 128)
     hipLaunchKernelGGL((segment_states_kernel<128, true>), dim3((unsigned)grid),
                        dim3(SS_WAVES * 64), 0, stream, (const __bf16 *)k, (const __bf16 *)v,

@@ -148,14 +148,22 @@ def test_split_validation(lib, kwargs):
 
 
 def test_split_workspace_size(lib):
-    def expect(T, S, H, D, nb):
+    def expect(T, S, H, D, nb, sub=1):
         a = lambda x: (x + 255) // 256 * 256
         cap = -(-T // (64 * nb)) + S - 1 if T > 0 else 0
-        return a(cap * H * D * D * 4) + a((cap + 1) * 4) + a((S + 1) * 4) + a(cap * 4)
+        return a(cap * sub * H * D * D * 4) + a((cap + 1) * 4) + a((S + 1) * 4) + a(cap * 4)
 
     for args in [(8192, 1, 8, 128, 16), (1000, 3, 2, 64, 1), (1, 1, 1, 128, 7), (0, 2, 4, 64, 2),
-                 (272568, 16, 64, 128, 64)]:
+                 (272568, 16, 64, 128, 64), (65536, 1, 16, 128, 256)]:
         assert lib.la_prefill_split_workspace_size(*args) == expect(*args), args
+    # sub-segment states of the bf16 two-launch form: one sequence in two segments, 64 heads x 2
+    # slices at d = 64 (128 workgroups; 512 fit one round) -> 4 sub-segments of 8,192 tokens;
+    # 32 heads x 4 slices at d = 128 (256 fit) -> 2; segments of 4,096 tokens over one head -> 2
+    # (sub-segments keep 2,048 tokens); 16,384 tokens in 8,192-token segments -> 4
+    for args, sub in [((65536, 1, 64, 64, 512), 4), ((65536, 1, 32, 128, 512), 2),
+                      ((8192, 1, 1, 128, 64), 2), ((16384, 1, 2, 64, 128), 4),
+                      ((65536, 1, 32, 64, 256), 2)]:
+        assert lib.la_prefill_split_workspace_size(*args) == expect(*args, sub=sub), args
     assert lib.la_prefill_split_workspace_size(100, 1, 1, 96, 4) == 0
     assert lib.la_prefill_split_workspace_size(100, 1, 1, 128, 0) == 0
 

@@ -225,3 +225,30 @@ def test_split_long_segment_kernels(D, seg_blocks):
     eg.append(float(state_errors(to_np(g[3]), want[3]).max()))
     print("  backward: dq %.2e dk %.2e dv %.2e d_init %.2e" % tuple(eg))
     assert max(eg) <= BF16_TOL
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_sub_segment_states(D):
+    """One sequence cut into two 8,192-token segments over two heads: too few segments before
+    the last to fill the device, so the two-launch state pass computes the first segment's
+    state as four 2,048-token sub-segment states that the second segment's prologue adds up.
+    Against the recurrent form, from an initial state, with the plain prefill beside it."""
+    T, H, seg_blocks = 16384, 2, 128
+    banner("split sub-segment states D=%d" % D)
+    d = dev()
+    q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=71)
+    decay = torch.tensor([0.999, 0.99995], dtype=torch.float32)
+    init = synth.random_state(1, H, D, seed=72, scale=0.1)
+    cu = synth.cu_from_lengths([T])
+    out, fs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d), cu.to(d),
+                         initial_state=init.to(d), split=seg_blocks)
+    po, pfs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d), cu.to(d),
+                         initial_state=init.to(d))
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(q, k, v, decay, cu, init_state=init)
+    e = slice_errors(to_np(out), ref, cu).max()
+    es = state_errors(to_np(fs), ref_s).max()
+    ep = slice_errors(to_np(po), ref, cu).max()
+    print("sub-segment states D=%d: out %.2e state %.2e (plain %.2e)" % (D, e, es, ep))
+    assert e <= BF16_TOL and es <= BF16_TOL and ep <= BF16_TOL
