@@ -290,16 +290,17 @@ def decode_tokens_leg(dev, iters=20, warmup=3):
 
 def few_chain_prefill(dev, iters=20, warmup=3):
     """Prefill shapes with fewer (sequence, head, 32-column slice) chains than compute units --
-    8,192 x 8 heads and 65,536 x 8 heads (one device's share of the 64-head layer under 8-way head
-    sharding) at d = 128, and the 64-head layer at d = 64 (two slices per head: 128 chains) --
-    timed with the plain scan and with the sequence split the library suggests."""
+    8,192 x 8 heads, 65,536 x 8 heads and 65,536 x 32 heads (one device's share of the 64-head
+    layer under 8-way and 2-way head sharding) at d = 128, and the 64-head layer at d = 64 (two
+    slices per head: 128 chains) -- timed with the plain scan and with the sequence split the
+    library suggests."""
     import torch
 
     import long_context_attention_attn_amd as la
     from long_context_attention_attn_amd import _lib, synth
 
     res = []
-    for T, Hc, Dh in ((8192, 8, D), (65536, 8, D), (65536, 64, 64)):
+    for T, Hc, Dh in ((8192, 8, D), (65536, 8, D), (65536, 32, D), (65536, 64, 64)):
         q, k, v = synth.qkv(T, Hc, Dh, torch.bfloat16, seed=0, device=dev)
         dec = synth.decay_geometric(Hc, 0.9, 0.9999).to(dev)
         o = torch.empty_like(q)
