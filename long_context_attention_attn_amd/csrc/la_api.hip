@@ -192,7 +192,8 @@ bool split_fused(int64_t T, int32_t H, int32_t D, int64_t seg_len) {
 // states.  A function of the sizes only, so the workspace size needs no device.
 int32_t split_sub(int64_t T, int32_t S, int32_t H, int32_t D, int64_t seg_len) {
   const int64_t segs = (T + seg_len - 1) / seg_len;  // segments of all sequences (at most)
-  const int64_t need = segs > S ? segs - S : 1;       // segments before a sequence's last
+  if (segs <= S) return 1;  // few sequences, if any, are cut: nothing to spread
+  const int64_t need = segs - S;                      // segments before a sequence's last
   const int64_t wgs = need * H * (D / 32), round = D == 64 ? 512 : 256;
   int32_t sub = 1;
   while (sub < 8 && wgs * sub * 2 <= round && seg_len % (sub * 2) == 0 &&

@@ -159,10 +159,12 @@ def test_split_workspace_size(lib):
     # sub-segment states of the bf16 two-launch form: one sequence in two segments, 64 heads x 2
     # slices at d = 64 (128 workgroups; 512 fit one round) -> 4 sub-segments of 8,192 tokens;
     # 32 heads x 4 slices at d = 128 (256 fit) -> 2; segments of 4,096 tokens over one head -> 2
-    # (sub-segments keep 2,048 tokens); 16,384 tokens in 8,192-token segments -> 4
+    # (sub-segments keep 2,048 tokens); 16,384 tokens in 8,192-token segments -> 4; no more
+    # segments than sequences (perhaps none cut) -> 1
     for args, sub in [((65536, 1, 64, 64, 512), 4), ((65536, 1, 32, 128, 512), 2),
                       ((8192, 1, 1, 128, 64), 2), ((16384, 1, 2, 64, 128), 4),
-                      ((65536, 1, 32, 64, 256), 2)]:
+                      ((65536, 1, 32, 64, 256), 2), ((15288, 3, 2, 128, 64), 2),
+                      ((18225, 5, 2, 128, 64), 1)]:
         assert lib.la_prefill_split_workspace_size(*args) == expect(*args, sub=sub), args
     assert lib.la_prefill_split_workspace_size(100, 1, 1, 96, 4) == 0
     assert lib.la_prefill_split_workspace_size(100, 1, 1, 128, 0) == 0

@@ -229,18 +229,22 @@ def test_split_long_segment_kernels(D, seg_blocks):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("D", [64, 128])
-def test_split_sub_segment_states(D):
-    """One sequence cut into two 8,192-token segments over two heads: too few segments before
-    the last to fill the device, so the two-launch state pass computes the first segment's
-    state as four 2,048-token sub-segment states that the second segment's prologue adds up.
-    Against the recurrent form, from an initial state, with the plain prefill beside it."""
-    T, H, seg_blocks = 16384, 2, 128
-    banner("split sub-segment states D=%d" % D)
+@pytest.mark.parametrize("lengths,seg_blocks", [([16384], 128), ([12288, 0, 3000], 64)])
+def test_split_sub_segment_states(D, lengths, seg_blocks):
+    """Too few segments before each sequence's last to fill the device, so the two-launch state
+    pass computes their states in sub-segments that the later segments' prologues add up: one
+    sequence in two 8,192-token segments (four 2,048-token sub-segments), and a packed batch
+    whose first sequence has three 4,096-token segments (two sub-segments each) beside an empty
+    and a one-segment sequence.  From initial states, against the recurrent form, with the plain
+    prefill beside it."""
+    H = 2
+    banner("split sub-segment states D=%d lengths=%s seg_blocks=%d" % (D, lengths, seg_blocks))
     d = dev()
+    cu = synth.cu_from_lengths(lengths)
+    T = int(cu[-1])
     q, k, v = synth.qkv(T, H, D, torch.bfloat16, seed=71)
     decay = torch.tensor([0.999, 0.99995], dtype=torch.float32)
-    init = synth.random_state(1, H, D, seed=72, scale=0.1)
-    cu = synth.cu_from_lengths([T])
+    init = synth.random_state(len(lengths), H, D, seed=72, scale=0.1)
     out, fs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d), cu.to(d),
                          initial_state=init.to(d), split=seg_blocks)
     po, pfs = la.prefill(q.to(d), k.to(d), v.to(d), decay.to(d), cu.to(d),
