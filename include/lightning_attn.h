@@ -200,7 +200,7 @@ size_t la_prefill_split_workspace_size(int64_t T, int32_t S, int32_t H, int32_t 
  * be cut), when a cost model of both paths (fitted to MI355X timings: per-block cost by dtype,
  * head size, workgroups in flight and whether q, k, v and out fit the 256 MB last-level cache;
  * the mean sequence length T / S stands in for the longest) predicts the split saves less than
- * 5% (short sequences, where its fixed cost of four launches dominates), or on any error. */
+ * 5% (short sequences, where its fixed cost of two or four launches dominates), or on any error. */
 int32_t la_prefill_split_blocks(int64_t T, int32_t S, int32_t H, int32_t D, la_dtype dtype);
 
 /* The same suggestion for a device with compute_units compute units (no device access; 0 for
