@@ -42,9 +42,9 @@
  * that for q and k (future scores are selected away, the state only carries a token forward),
  * but a block's matrix products multiply the masked-out (exactly zero) weights by v on the
  * matrix cores, and 0 * inf or 0 * NaN is NaN there.  So a non-finite v at token t reaches
- * earlier outputs of its own 64-token block (within the 32-token operand group of the intra
- * product in bf16, the 16-token tile in fp32), never those of an earlier block nor anything
- * before the sequence's start.
+ * earlier outputs of its own block (within the 32-token operand group of the intra product in
+ * bf16, at either block size; the 16-token tile in fp32), never those of an earlier block nor
+ * anything before the sequence's start.
  *
  * Errors.  Argument checks run on the host before any HIP call and return a status; nothing
  * throws across this ABI.  Device data is not validated: non-monotone cu_seqlens or lambda
