@@ -173,8 +173,10 @@ la_status la_prefill_split(const void *q, const void *k, const void *v, const fl
  * load until the process ends.  The call allocates nothing (no hipMalloc, no hipFree, no
  * allocating library routine); the caller still owns every other buffer.  Same arguments,
  * result and errors as la_prefill_split otherwise, plus LA_ERR_INVALID_ARG when these sizes
- * need more than LA_SPLIT_STATIC_SCRATCH_BYTES of workspace
- * (la_prefill_split_workspace_size(T, S, H, D, seg_blocks) > LA_SPLIT_STATIC_SCRATCH_BYTES).
+ * need more than LA_SPLIT_STATIC_SCRATCH_BYTES of workspace even with one state per segment
+ * (the call keeps no sub-segment states when they would not fit; sizes with
+ * la_prefill_split_workspace_size(T, S, H, D, seg_blocks) <= LA_SPLIT_STATIC_SCRATCH_BYTES
+ * always fit).
  * All calls on one device share its scratch: calls that overlap in time on one device (two
  * streams, two host threads) race and give wrong results; order them on one stream.  The
  * scratch needs no initial contents.

@@ -70,7 +70,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tens
     gives the same result up to rounding.
     static_scratch: with a sequence split, keep its segment states in the library's static
     device scratch (la_prefill_split_static) instead of a torch-allocated workspace, so the
-    library call allocates nothing; needs la_prefill_split_workspace_size <= 32 MiB.  Calls
+    library call allocates nothing; sizes with la_prefill_split_workspace_size <= 32 MiB
+    always fit (larger ones fit if one state per segment does).  Calls
     that overlap in time on one device share that scratch and must be ordered on one stream.
     """
     device = q.device
