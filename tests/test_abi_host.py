@@ -420,6 +420,29 @@ def test_split_static_limit(lib):
     assert b"static scratch" in lib.la_last_error()
 
 
+def test_split_static_falls_back_to_one_state_per_segment(lib):
+    """8 sequences of ~36,864 tokens x 16 heads in 32,768-token segments (two per sequence):
+    the bf16 two-launch form would keep 2 sub-segment states per segment (32 MiB of states, past
+    the scratch); the static call keeps one per segment (16 MiB) instead, so without a device it
+    gets past the size check and fails only at the device check."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    from long_context_attention_attn_amd import _lib
+
+    T, S, H, D, nb = 294912, 8, 16, 128, 512
+    assert lib.la_prefill_split_workspace_size(T, S, H, D, nb) > _lib.SPLIT_STATIC_SCRATCH_BYTES
+    GiB = 1 << 30
+    q, k, v = (ctypes.c_void_p(x * GiB) for x in (16, 20, 24))  # 2.4 GB each at fp32
+    out, cu = ctypes.c_void_p(28 * GiB), ctypes.c_void_p(32 * GiB)
+    st = lib.la_prefill_split_static(q, k, v, P, cu, None, out, None, T, S, H, D, 1, nb, None)
+    assert st == 3, lib.la_last_error()
+    # fp32 storage has no sub-segment states: the same sizes fit as they are
+    assert lib.la_prefill_split_static(q, k, v, P, cu, None, out, None, T, S, H, D, 0, nb,
+                                       None) == 3
+
+
 def test_split_static_without_device(lib):
     import torch
 
