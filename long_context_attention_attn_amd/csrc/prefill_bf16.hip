@@ -575,22 +575,22 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
   c.s0t = flags & 4;
 
   const int tid = threadIdx.x;
+  const float lam = decay[h];
+  // The split form's incoming-state loads go out first, in flight during the LDS zeroing and
+  // the powers table.
+  IncomingState<D, CV, NTHR> incoming;
+  if constexpr (SPLIT) incoming.issue(s0, seg_states, sp, sub, H, h, c.c0, tid);
   // Zero the stages once: rows a partial block does not load then hold zeros or finite values
   // of earlier blocks, never stale bits from another kernel.
   for (int off = 16 * tid; off < NST * C::STAGE; off += 16 * NTHR)
     *(u32x4 *)(smem + off) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
-  if (tid <= BLK) {
-    const float lam = decay[h];
-    double p = 1.0;  // lambda^tid by repeated multiplication (0^0 = 1)
-    for (int i = 0; i < tid; ++i) p *= (double)lam;
-    pw[tid] = (float)p;
-  }
+  if (tid <= BLK) pw[tid] = seg_decay(lam, tid);  // lambda^tid in fp64 (0^0 = 1), then fp32
   __syncthreads();  // pw and zeroed stages visible before any DMA or read
   size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   if constexpr (SPLIT) {
-    split_incoming_state<D, CV, NTHR>((float *)(smem + SIN_OFF<D>()), s0, seg_states, sp, sub,
-                                      H, h, c.c0, seg_decay(decay[h], seg_len / sub), tid);
+    incoming.finish((float *)(smem + SIN_OFF<D>()), seg_states, sp, sub, H, h, c.c0,
+                    seg_decay(lam, seg_len / sub), tid);
     __syncthreads();
     // the final state is the sequence's, written by its last segment only
     sbase = ((size_t)sp.seq * H + h) * (size_t)D * D;

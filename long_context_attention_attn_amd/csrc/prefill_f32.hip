@@ -30,6 +30,7 @@
 // incl_v[s] != 0 when incl_v is given), a transposed initial state, and a state-only pass that
 // reads no q and writes no out.
 #include "la_internal.h"
+#include "seg_lookup.h"
 
 namespace {
 
@@ -449,12 +450,7 @@ __global__ __launch_bounds__(NTHR) void prefill_f32_kernel(
   x.s0t = flags & 4;
   x.so = flags & 8;
   const int tid = threadIdx.x;
-  if (tid <= BLK) {
-    const float lam = decay[h];
-    double p = 1.0;  // lambda^tid by repeated multiplication (0^0 = 1)
-    for (int i = 0; i < tid; ++i) p *= (double)lam;
-    sm.pw[tid] = (float)p;
-  }
+  if (tid <= BLK) sm.pw[tid] = seg_decay(decay[h], tid);  // lambda^tid in fp64 (0^0 = 1), then fp32
   // pw is made visible by the barrier that follows the first block's staging.
   const size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   // Waves w and w + 4 share a SIMD: output wave r pairs with the state wave holding the most

@@ -94,26 +94,25 @@ __device__ __forceinline__ float seg_decay(float lam, int64_t m) {
 // in fp32 with one fmaf per step (for sub = 1 the rounding of a separate combine pass).
 // s0: [S][H][D][D] or nullptr; states: [slots * sub][H][D][D]; sin: the [D][CV] fp32 result
 // (LDS); lam_l = lambda^(L/sub).
+// Two phases, so that the loads are in flight while the workgroup does its other prologue
+// work: issue() loads the initial state and the first NB earlier states into registers;
+// finish() adds them up (loading any further states in batches of NB) and stores S_in.
 template <int D, int CV, int NTHR>
-__device__ __forceinline__ void split_incoming_state(float *sin, const float *s0,
-                                                     const float *states, const SegPos &sp,
-                                                     int sub, int H, int h, int c0, float lam_l,
-                                                     int tid) {
+struct IncomingState {
   typedef __attribute__((ext_vector_type(4))) float f4;
-  constexpr int E = D * CV / NTHR;  // elements per thread, consecutive columns
+  static constexpr int E = D * CV / NTHR;  // elements per thread, consecutive columns
+  static constexpr int NB = 8;             // earlier states loaded per batch, all in flight
   static_assert(E % 4 == 0 && CV % E == 0, "whole 16-byte pieces of one row per thread");
-  const int e0 = tid * E, dk = e0 / CV, col = e0 % CV;
-  const size_t off = (size_t)dk * D + c0 + col;
-  const size_t DD = (size_t)D * D;
   float acc[E];
-  const float *src0 = s0 ? s0 + ((size_t)sp.seq * H + h) * DD + off : nullptr;
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = src0 ? src0[e] : 0.f;
-  constexpr int NB = 8;  // earlier states loaded per batch, all loads in flight together
-  const int nx = sp.j * sub;                 // sub-segment states before segment j
-  const size_t x0 = (size_t)sp.first * sub;  // slot of the sequence's first one
-  for (int jb = 0; jb < nx; jb += NB) {
-    f4 buf[NB][E / 4];
+  f4 buf[NB][E / 4];
+
+  __device__ __forceinline__ static size_t offset(int c0, int tid) {
+    const int e0 = tid * E;
+    return (size_t)(e0 / CV) * D + c0 + e0 % CV;
+  }
+  __device__ __forceinline__ void load_batch(const float *states, size_t x0, int jb, int nx, int H,
+                                             int h, size_t off) {
+    const size_t DD = (size_t)D * D;
 #pragma unroll
     for (int x = 0; x < NB; ++x)
       if (jb + x < nx) {
@@ -121,6 +120,8 @@ __device__ __forceinline__ void split_incoming_state(float *sin, const float *s0
 #pragma unroll
         for (int u = 0; u < E / 4; ++u) buf[x][u] = *(const f4 *)(p + 4 * u);
       }
+  }
+  __device__ __forceinline__ void add_batch(int jb, int nx, float lam_l) {
 #pragma unroll
     for (int x = 0; x < NB; ++x)
       if (jb + x < nx) {
@@ -130,6 +131,24 @@ __device__ __forceinline__ void split_incoming_state(float *sin, const float *s0
           for (int e = 0; e < 4; ++e) acc[4 * u + e] = fmaf(lam_l, acc[4 * u + e], buf[x][u][e]);
       }
   }
+  __device__ __forceinline__ void issue(const float *s0, const float *states, const SegPos &sp,
+                                        int sub, int H, int h, int c0, int tid) {
+    const size_t off = offset(c0, tid);
+    const float *src0 = s0 ? s0 + ((size_t)sp.seq * H + h) * ((size_t)D * D) + off : nullptr;
 #pragma unroll
-  for (int e = 0; e < E; ++e) sin[e0 + e] = acc[e];
-}
+    for (int e = 0; e < E; ++e) acc[e] = src0 ? src0[e] : 0.f;
+    load_batch(states, (size_t)sp.first * sub, 0, sp.j * sub, H, h, off);
+  }
+  __device__ __forceinline__ void finish(float *sin, const float *states, const SegPos &sp,
+                                         int sub, int H, int h, int c0, float lam_l, int tid) {
+    const size_t off = offset(c0, tid), x0 = (size_t)sp.first * sub;
+    const int nx = sp.j * sub;  // sub-segment states before segment j
+    add_batch(0, nx, lam_l);
+    for (int jb = NB; jb < nx; jb += NB) {
+      load_batch(states, x0, jb, nx, H, h, off);
+      add_batch(jb, nx, lam_l);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) sin[tid * E + e] = acc[e];
+  }
+};
