@@ -321,6 +321,12 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, base + voff[u], 0, 0));
   };
 
+  // The first two chunks' loads go out before the weights are computed (lambda was requested
+  // first), so the powers below are formed while they are in flight.
+  if (ch_hi >= 0) {
+    fetch(ch_hi, kreg[0], vreg[0]);
+    fetch(ch_hi - SS_WAVES >= 0 ? ch_hi - SS_WAVES : ch_hi, kreg[1], vreg[1]);
+  }
   // Weights of this lane's V rows in the current chunk (fp64), times wstep[u] after each step.
   // A row past the end of the wave's first chunk (a partial last chunk of the segment; its data
   // reads as zero there) starts at its weight in the wave's next chunk, lambda^(e+256), and
@@ -334,8 +340,6 @@ __global__ __launch_bounds__(SS_WAVES * 64) void segment_states_kernel(
       wv[u] = powd(lam, e >= 0 ? e : e + SS_CH * SS_WAVES);
       wstep[u] = e >= 0 ? lam256 : 1.0;
     }
-    fetch(ch_hi, kreg[0], vreg[0]);
-    fetch(ch_hi - SS_WAVES >= 0 ? ch_hi - SS_WAVES : ch_hi, kreg[1], vreg[1]);
   }
 
   // One chunk: stage it from register set (kd, vd), refill the set with the chunk two steps
