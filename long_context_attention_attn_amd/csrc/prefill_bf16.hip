@@ -586,16 +586,16 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_bf16_kernel(
     *(u32x4 *)(smem + off) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
   if (tid <= BLK) pw[tid] = seg_decay(lam, tid);  // lambda^tid in fp64 (0^0 = 1), then fp32
-  __syncthreads();  // pw and zeroed stages visible before any DMA or read
   size_t sbase = ((size_t)seq * H + h) * (size_t)D * D;
   if constexpr (SPLIT) {
+    // S_in lies past the powers table, in the zeroed stages: it needs no barrier of its own
     incoming.finish((float *)(smem + SIN_OFF<D>()), seg_states, sp, sub, H, h, c.c0,
                     seg_decay(lam, seg_len / sub), tid);
-    __syncthreads();
     // the final state is the sequence's, written by its last segment only
     sbase = ((size_t)sp.seq * H + h) * (size_t)D * D;
     if (sp.j != sp.count - 1) fs = nullptr;
   }
+  __syncthreads();  // the powers, S_in and the zeroed stages visible before any copy or read
   const int lane = tid & 63;
   switch (tid >> 6) {
     case 0: output_wave<D, 0, SO, REV>(c, smem, pw, lane); break;
