@@ -81,7 +81,7 @@ struct Cfg : RowCfg<D> {
 };
 
 // LDS offset of the incoming state of a segment in the sequence-split form (see
-// split_incoming_state): after the powers table in the last stage.
+// IncomingState in seg_lookup.h): after the powers table in the last stage.
 template <int D>
 constexpr int SIN_OFF() { return (NST - 1) * Cfg<D>::STAGE + 1024; }
 

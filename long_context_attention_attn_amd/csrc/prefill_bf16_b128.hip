@@ -67,7 +67,7 @@ struct Cfg : RowCfg<D> {
 
 // Sequence-split form (SPLIT): one workgroup per segment slot of la_prefill_split's segment
 // numbering (seg_lookup.h), which finds its segment and forms its incoming state in the
-// prologue from the states the segment-state pass left (split_incoming_state).  The slice's
+// prologue from the states the segment-state pass left (IncomingState).  The slice's
 // incoming state (D x 32 fp32) reaches the state waves through LDS, after the powers table in
 // stage 1, which the first copies into that stage (step 0, after the prologue barrier) overwrite.
 template <int D>
