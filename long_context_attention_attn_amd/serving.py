@@ -72,7 +72,8 @@ class GraphedPrefill:
     buffers, valid until the next call.  Not thread-safe; one stream."""
 
     def __init__(self, T_pad: int, S_pad: int, H: int, D: int, dtype=torch.bfloat16,
-                 device="cuda", with_initial_state: bool = False, split=None):
+                 device="cuda", with_initial_state: bool = False, split=None,
+                 static_scratch: bool = False):
         self.T_pad, self.S_pad, self.H, self.D = T_pad, S_pad, H, D
         dev = torch.device(device)
         self.q = torch.zeros((T_pad, H, D), dtype=dtype, device=dev)
@@ -85,6 +86,10 @@ class GraphedPrefill:
                      if with_initial_state else None)
         self.final_state = torch.empty((S_pad, H, D, D), dtype=torch.float32, device=dev)
         self._split = split
+        # with a split: keep the segment states in the library's static scratch, so the captured
+        # launches allocate nothing (no workspace from the graph's memory pool); replays of
+        # graphs that share one device's scratch must not overlap in time
+        self._static = static_scratch
         self.cu[:] = torch.tensor([0] + [T_pad] * S_pad, dtype=torch.int32)
         # warm up (library load, device check) outside the capture
         s = torch.cuda.Stream(device=dev)
@@ -99,7 +104,8 @@ class GraphedPrefill:
 
     def _launch(self):
         prefill(self.q, self.k, self.v, self.decay, self.cu, initial_state=self.init,
-                out=self.out, final_state=self.final_state, split=self._split)
+                out=self.out, final_state=self.final_state, split=self._split,
+                static_scratch=self._static)
 
     def __call__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: torch.Tensor,
                  lengths: Sequence[int], initial_state: Optional[torch.Tensor] = None):
